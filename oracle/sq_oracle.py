@@ -1,0 +1,467 @@
+"""Plain CPU fp64 oracle for the SquareQ v3 W4 linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares
+no code with the device library and never imports it.
+
+Source: the SquareQ README (github.itlym.cn/CodeAlexx/SquareQ), section
+"SquareQ v3 - W4 (Hadamard-256 + low-rank + int4 / NVFP4)":
+
+* the weight is the sum of a bf16 low-rank product lora_up @ lora_down^T
+  and the inverse block Hadamard-256 rotation of a dequantized residual
+  (the format formula at the top of the section);
+* the rotation is a block-diagonal normalized Hadamard-256 over the input
+  dimension, for any K divisible by 256 (the "Rotation" bullet);
+* the residual codec is int4 with group-32 or group-64 scales whose
+  fraction is chosen by an MSE sweep (the "Residual codecs" bullet; the
+  sweep grid f in {0.70, 0.71, ..., 1.00} with scale f*absmax/7 and codes
+  in [-8, 7] is the one the layer configurations state);
+* the low-rank branch is a rank-32 SVD of the weight, stored in bf16 (the
+  "Low-rank branch" bullet);
+* the selftest gates named in the "Layout" paragraph (pack/unpack
+  bit-exact, rotation self-inverse, determinism) are among the pins.
+
+Everything is numpy float64; LAPACK SVD and BLAS matmul are the only
+library primitives.  Points the page leaves open are decided as follows
+(each decision is repeated where it is used):
+
+  R1 Hadamard order: Sylvester, S[i,j] = (-1)^popcount(i & j); H = S/16.
+  R2 side: each row is rotated along K; R = E @ H (H symmetric, H @ H = I).
+  R3 SVD split: up = U*sqrt(S), down = V*sqrt(S), rounded to bf16 straight
+     from fp64; the residual is taken against the rounded factors.
+  R4 scales are stored as IEEE fp16; each candidate scale is rounded to
+     fp16 before its codes and error are computed.
+  R5 codes: round half to even, clamp to [-8, 7]; a zero scale gives code 0.
+  R6 the sweep minimises the sum of squared errors in the rotated domain;
+     ties go to the lowest fraction index.
+  R7 packing: byte b = (q[2b] & 0xF) | (q[2b+1] & 0xF) << 4, two's complement.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+HBLOCK = 256
+N_FRAC = 31          # f = 0.70 ... 1.00 in steps of 0.01
+QMIN, QMAX = -8, 7
+
+
+# --------------------------------------------------------------------------
+# floating-point formats (written from the IEEE definitions)
+# --------------------------------------------------------------------------
+def _round_to_format(x, sig_bits: int, emin: int, max_finite: float) -> np.ndarray:
+    """Round fp64 values to a binary format with ``sig_bits`` significant bits.
+
+    Round to nearest, ties to even, with gradual underflow below 2**emin and
+    overflow to +-inf when the rounded magnitude exceeds ``max_finite``.
+    One rounding straight from fp64 (no intermediate format).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    fin = np.isfinite(x) & (x != 0)
+    m, e = np.frexp(x[fin])                      # x = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e, emin + 1)                  # subnormal range: fixed spacing
+    spacing = np.ldexp(1.0, e - sig_bits)
+    r = np.rint(x[fin] / spacing) * spacing      # division by a power of two: exact
+    r = np.where(np.abs(r) > max_finite, np.copysign(np.inf, r), r)
+    out[fin] = r
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out
+
+
+def fp16_round(x) -> np.ndarray:
+    """IEEE binary16 round-to-nearest-even of fp64 values (returned as fp64)."""
+    return _round_to_format(x, 11, -14, 65504.0)
+
+
+def bf16_round(x) -> np.ndarray:
+    """bfloat16 round-to-nearest-even of fp64 values (returned as fp64)."""
+    return _round_to_format(x, 8, -126, float.fromhex("0x1.fep127"))
+
+
+def bf16_decode(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> fp64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def fp16_decode(h) -> np.ndarray:
+    """fp16 array or uint16 bit patterns -> fp64 values."""
+    h = np.asarray(h)
+    if h.dtype == np.uint16:
+        h = h.view(np.float16)
+    return h.astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# Hadamard-256 (the "Rotation" bullet; readings R1, R2)
+# --------------------------------------------------------------------------
+def sylvester(n: int = HBLOCK) -> np.ndarray:
+    """S[i,j] = (-1)^popcount(i & j), the natural-order Sylvester matrix."""
+    i = np.arange(n)
+    pc = np.vectorize(lambda v: bin(v).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+_H = None
+
+
+def hadamard256() -> np.ndarray:
+    """Normalized Hadamard-256: H = S/16, symmetric and its own inverse."""
+    global _H
+    if _H is None:
+        _H = sylvester(HBLOCK) / 16.0
+    return _H
+
+
+def rotate(a) -> np.ndarray:
+    """Apply the block-diagonal H to every row: out[:, 256b:256b+256] = a[:, block b] @ H.
+
+    K must be a multiple of 256.  The same map is its own inverse.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    k = a.shape[-1]
+    if k % HBLOCK:
+        raise ValueError("K must be a multiple of 256")
+    blocks = a.reshape(a.shape[:-1] + (k // HBLOCK, HBLOCK))
+    return (blocks @ hadamard256()).reshape(a.shape)
+
+
+def fwht_fast(a) -> np.ndarray:
+    """The same rotation through radix-2 butterflies (a+b, a-b), then x 1/16.
+
+    Independent of the dense matrix above; used to cross-check it.
+    """
+    a = np.array(a, dtype=np.float64, copy=True)
+    k = a.shape[-1]
+    v = a.reshape(-1, k // HBLOCK, HBLOCK)
+    h = 1
+    while h < HBLOCK:
+        v = v.reshape(v.shape[0], v.shape[1], HBLOCK // (2 * h), 2, h)
+        lo = v[:, :, :, 0, :].copy()
+        hi = v[:, :, :, 1, :].copy()
+        v[:, :, :, 0, :] = lo + hi
+        v[:, :, :, 1, :] = lo - hi
+        h *= 2
+    return (v.reshape(a.shape) / 16.0)
+
+
+# --------------------------------------------------------------------------
+# low-rank branch (the "Low-rank branch" bullet; reading R3)
+# --------------------------------------------------------------------------
+def svd_init(w, rank: int = 32, round_bf16: bool = True):
+    """Rank-``rank`` split of W: up = U_r sqrt(S_r), down = V_r sqrt(S_r), bf16-rounded.
+
+    Returns (up [N,r], down [K,r]) as fp64 arrays holding bf16 values
+    (unrounded when ``round_bf16`` is False, for the Eckart-Young pin).
+    Only the product up @ down^T is meaningful (signs of singular vectors
+    are arbitrary).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    if rank == 0:
+        return np.zeros((w.shape[0], 0)), np.zeros((w.shape[1], 0))
+    u, s, vt = np.linalg.svd(w, full_matrices=False)
+    r = np.sqrt(s[:rank])
+    up = u[:, :rank] * r
+    down = vt[:rank].T * r
+    if round_bf16:
+        up, down = bf16_round(up), bf16_round(down)
+    return up, down
+
+
+def residual(w, up, down) -> np.ndarray:
+    """Rotated residual R = rotate(W - up @ down^T) (format formula, reading R2)."""
+    w = np.asarray(w, dtype=np.float64)
+    e = w - np.asarray(up, np.float64) @ np.asarray(down, np.float64).T
+    return rotate(e)
+
+
+# --------------------------------------------------------------------------
+# int4 codec with MSE-swept fractional scales (the "Residual codecs" bullet)
+# --------------------------------------------------------------------------
+def fractions_grid() -> np.ndarray:
+    """The 31 candidate fractions f_i = (70 + i)/100."""
+    return (70 + np.arange(N_FRAC)) / 100.0
+
+
+def candidate_scale_exact(absmax, i):
+    """Unrounded candidate scale f_i * absmax / 7 = (70+i)*absmax/700 (fp64)."""
+    return (70.0 + i) * np.asarray(absmax, np.float64) / 700.0
+
+
+def codes_for_scale(r, s) -> np.ndarray:
+    """Reading R5: q = clamp(round_half_even(r/s), -8, 7); q = 0 where s == 0."""
+    r = np.asarray(r, np.float64)
+    s = np.asarray(s, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.clip(np.rint(r / s), QMIN, QMAX)
+    return np.where(s == 0, 0.0, q)
+
+
+@dataclass
+class QuantResult:
+    q: np.ndarray        # int codes [N,K] (int8)
+    scale: np.ndarray    # fp16 scale values [N,K/G] (float64 holding fp16 values)
+    fidx: np.ndarray     # chosen fraction index [N,K/G] (uint8)
+    mse: np.ndarray      # [N,K/G,31] sum of squared errors per candidate
+    absmax: np.ndarray   # [N,K/G]
+
+
+def quantize_residual(r, group: int) -> QuantResult:
+    """Sweep the 31 fractions for every group of ``group`` values along K.
+
+    For group values r_1..r_G with absmax a, candidate i uses
+    s_i = fp16(f_i a / 7) (reading R4), codes q = clamp(rint(r/s_i), -8, 7)
+    (R5) and error sum (r - q s_i)^2; the chosen index is the first
+    minimiser (R6).  Non-finite inputs or an fp16 scale overflow raise.
+    """
+    r = np.asarray(r, np.float64)
+    n, k = r.shape
+    if group not in (32, 64) or k % HBLOCK:
+        raise ValueError("group must be 32 or 64 and K a multiple of 256")
+    if not np.all(np.isfinite(r)):
+        raise FloatingPointError("non-finite residual")
+    rg = r.reshape(n, k // group, group)
+    a = np.abs(rg).max(axis=2)
+    mse = np.empty((n, k // group, N_FRAC))
+    scales = np.empty((n, k // group, N_FRAC))
+    for i in range(N_FRAC):
+        s = fp16_round(candidate_scale_exact(a, i))
+        if np.any(np.isinf(s)):
+            raise FloatingPointError("fp16 scale overflow")
+        q = codes_for_scale(rg, s[..., None])
+        mse[..., i] = ((rg - q * s[..., None]) ** 2).sum(axis=2)
+        scales[..., i] = s
+    best = np.argmin(mse, axis=2)          # numpy argmin returns the first minimum
+    s_best = np.take_along_axis(scales, best[..., None], axis=2)[..., 0]
+    q_best = codes_for_scale(rg, s_best[..., None]).reshape(n, k)
+    return QuantResult(q_best.astype(np.int8), s_best, best.astype(np.uint8), mse, a)
+
+
+def quantize_weight(w, up, down, group: int) -> QuantResult:
+    """Builder path: residual against the bf16 factors, rotation, sweep."""
+    return quantize_residual(residual(w, up, down), group)
+
+
+def pack(q) -> np.ndarray:
+    """Reading R7: two's-complement nibbles, even k in the low nibble."""
+    q = np.asarray(q).astype(np.int64)
+    if q.shape[-1] % 2:
+        raise ValueError("even K required")
+    lo = q[..., 0::2] & 0xF
+    hi = q[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack(codes) -> np.ndarray:
+    """Inverse of ``pack``: uint8 [N,K/2] -> int8 [N,K] in [-8, 7]."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    lo = c & 0xF
+    hi = c >> 4
+    q = np.empty(c.shape[:-1] + (2 * c.shape[-1],), dtype=np.int64)
+    q[..., 0::2] = lo
+    q[..., 1::2] = hi
+    q = np.where(q >= 8, q - 16, q)
+    return q.astype(np.int8)
+
+
+def dequant(q, scale, group: int) -> np.ndarray:
+    """D = q * s with s repeated over each group (exact in fp64)."""
+    q = np.asarray(q, np.float64)
+    s = np.repeat(np.asarray(scale, np.float64), group, axis=-1)
+    return q * s
+
+
+# --------------------------------------------------------------------------
+# the layer (format formula)
+# --------------------------------------------------------------------------
+def reconstruct(q, scale, up, down, group: int) -> np.ndarray:
+    """W_hat = up @ down^T + rotate(dequant(R)) in fp64 (format formula)."""
+    lr = np.asarray(up, np.float64) @ np.asarray(down, np.float64).T
+    return lr + rotate(dequant(q, scale, group))
+
+
+def forward(x, q, scale, up, down, group: int) -> np.ndarray:
+    """y = x @ W_hat^T = rotate(x) @ D^T + (x @ down) @ up^T in fp64.
+
+    The two halves follow from the format formula: H is symmetric, so
+    x @ (D H)^T = (x H) @ D^T.
+    """
+    x = np.asarray(x, np.float64)
+    d = dequant(q, scale, group)
+    return rotate(x) @ d.T + (x @ np.asarray(down, np.float64)) @ np.asarray(up, np.float64).T
+
+
+def forward_fp16_operands(x, q, scale, up, down, group: int) -> np.ndarray:
+    """Diagnostic forward: the contraction's operands rounded to fp16.
+
+    The rotated activations of each row are multiplied by the power of two
+    2^(11-E), E = ceil(log2(max|x_row|)) (so every |x H| <= 16 max|x| maps
+    below 2^15), rounded to fp16, and the dequantized weight is rounded to
+    fp16 (q*s rounded once); the row factor is undone afterwards and the
+    low-rank term is exact.  A device contraction on fp16 operands with fp32
+    accumulation should agree with this to accumulation-order error.
+    """
+    x = np.asarray(x, np.float64)
+    xh = rotate(x)
+    amax = np.abs(x).max(axis=1)
+    e = np.zeros(x.shape[0])
+    nz = amax > 0
+    # smallest E with amax <= 2**E
+    mant, ex = np.frexp(amax[nz])
+    e[nz] = np.where(mant == 0.5, ex - 1, ex)
+    f = np.ldexp(1.0, (11 - e).astype(np.int64))
+    xh16 = fp16_round(xh * f[:, None])
+    d16 = fp16_round(dequant(q, scale, group))
+    y = (xh16 @ d16.T) / f[:, None]
+    return y + (x @ np.asarray(down, np.float64)) @ np.asarray(up, np.float64).T
+
+
+# --------------------------------------------------------------------------
+# metrics
+# --------------------------------------------------------------------------
+def rel_fro(a, b) -> float:
+    """||a - b||_F / ||b||_F over the flattened arrays, fp64."""
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb else float(np.linalg.norm(a))
+
+
+def cosine(a, b) -> float:
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+# --------------------------------------------------------------------------
+# tie certification for comparing a fp32 device quantizer with this oracle
+# --------------------------------------------------------------------------
+SCALE_MARGIN = 1e-5   # relative distance of f*a/7 from an fp16 rounding boundary
+CODE_MARGIN = 2e-4    # distance of r/s from a half-integer, in code units
+SWEEP_MARGIN = 1e-4   # relative gap between best and any other candidate
+
+
+def _fp16_bracket(v):
+    """(lo, hi): the fp16 values with lo <= v <= hi that are adjacent (v >= 0)."""
+    v = np.asarray(v, np.float64)
+    s = fp16_round(v).astype(np.float16)
+    up = np.nextafter(s, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(s, np.float16(0)).astype(np.float64)
+    s = s.astype(np.float64)
+    lo = np.where(s <= v, s, dn)
+    hi = np.where(s >= v, s, up)
+    return lo, hi
+
+
+def _fp16_boundary_margin(v) -> np.ndarray:
+    """Relative distance of v (>= 0) from the nearest fp16 rounding boundary.
+
+    The boundaries around v are the midpoints between the fp16 value that
+    v rounds to and its two neighbours.
+    """
+    v = np.asarray(v, np.float64)
+    s16 = fp16_round(v).astype(np.float16)
+    s = s16.astype(np.float64)
+    up = np.nextafter(s16, np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(s16, np.float16(0)).astype(np.float64)
+    d = np.minimum(np.abs(v - (s + up) / 2), np.abs(v - (s + dn) / 2))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out = np.where(v > 0, d / np.where(v > 0, v, 1), np.inf)
+    return out
+
+
+def certify(r, res: QuantResult, group: int):
+    """Per-group flag: True where the oracle's choice is far from every tie.
+
+    A group is certified when (a) the chosen unrounded scale is at least
+    SCALE_MARGIN (relative) from an fp16 rounding boundary, (b) every r/s
+    is at least CODE_MARGIN from a half-integer, and (c) every other
+    candidate's error exceeds the best by SWEEP_MARGIN (relative), also when
+    that candidate's scale would round the other way.  A device quantizer
+    whose residual differs from the oracle's by fp32 rounding must then
+    reproduce codes, scale and index bit for bit.
+    """
+    r = np.asarray(r, np.float64)
+    n, k = r.shape
+    rg = r.reshape(n, k // group, group)
+    a = res.absmax
+    best = res.fidx.astype(np.int64)
+    v_best = candidate_scale_exact(a, best)
+    ok = _fp16_boundary_margin(v_best) > SCALE_MARGIN
+    ok |= (a == 0)
+    s = res.scale[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(s > 0, rg / np.where(s > 0, s, 1), 0.0)
+    frac = np.abs(t - np.floor(t) - 0.5)
+    near = (frac < CODE_MARGIN) & (t > QMIN - 1) & (t < QMAX + 1)
+    ok &= ~near.any(axis=2)
+    # sweep margin, including the alternative rounding of ambiguous scales
+    mse_min_other = np.full(a.shape, np.inf)
+    for i in range(N_FRAC):
+        v = candidate_scale_exact(a, i)
+        variants = [fp16_round(v)]
+        amb = _fp16_boundary_margin(v) <= SCALE_MARGIN
+        if np.any(amb):
+            lo, hi = _fp16_bracket(v)
+            variants.append(np.where(amb, lo, variants[0]))
+            variants.append(np.where(amb, hi, variants[0]))
+        for sv in variants:
+            q = codes_for_scale(rg, sv[..., None])
+            m = ((rg - q * sv[..., None]) ** 2).sum(axis=2)
+            is_best = (best == i) & (sv == res.scale)
+            mse_min_other = np.where(is_best, mse_min_other, np.minimum(mse_min_other, m))
+    mse_best = np.take_along_axis(res.mse, best[..., None], axis=2)[..., 0]
+    gap_ok = mse_min_other > mse_best * (1 + SWEEP_MARGIN)
+    gap_ok |= (a == 0)
+    return ok & gap_ok
+
+
+def check_device_quant(r, res: QuantResult, group: int, q_dev, scale_dev, fidx_dev):
+    """Compare a device quantization with the oracle under tie certification.
+
+    Returns a dict with counts; ``ok`` is True when certified groups match
+    bit for bit and every uncertified group is an admissible near-tie:
+    its scale is one of the two fp16 neighbours of f_j a/7 for the device's
+    index j, its codes are the requantization with that scale except for
+    values within CODE_MARGIN of a half-integer (which may take either
+    neighbour), and its error is within SWEEP_MARGIN of the best.
+    """
+    r = np.asarray(r, np.float64)
+    n, k = r.shape
+    ng = k // group
+    rg = r.reshape(n, ng, group)
+    cert = certify(r, res, group)
+    qd = np.asarray(q_dev).astype(np.int64).reshape(n, ng, group)
+    qo = res.q.astype(np.int64).reshape(n, ng, group)
+    sd = np.asarray(scale_dev, np.float64)
+    fd = np.asarray(fidx_dev).astype(np.int64)
+    same = (fd == res.fidx) & (sd == res.scale) & (qd == qo).all(axis=2)
+    bad_cert = cert & ~same
+    # admissibility of every group that differs
+    v = candidate_scale_exact(res.absmax, fd)
+    lo, hi = _fp16_bracket(v)
+    scale_ok = (sd == lo) | (sd == hi)
+    scale_ok |= (res.absmax == 0) & (sd == 0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(sd[..., None] > 0, rg / np.where(sd[..., None] > 0, sd[..., None], 1), 0.0)
+    q_req = np.clip(np.rint(t), QMIN, QMAX)
+    frac = np.abs(t - np.floor(t) - 0.5)
+    near = frac < CODE_MARGIN
+    q_lo = np.clip(np.floor(t), QMIN, QMAX)
+    q_hi = np.clip(np.ceil(t), QMIN, QMAX)
+    codes_ok = ((qd == q_req) | (near & ((qd == q_lo) | (qd == q_hi)))).all(axis=2)
+    mse_dev = ((rg - qd * sd[..., None]) ** 2).sum(axis=2)
+    mse_best = np.take_along_axis(res.mse, res.fidx[..., None].astype(np.int64), axis=2)[..., 0]
+    err_ok = mse_dev <= mse_best * (1 + SWEEP_MARGIN) + 1e-300
+    admissible = scale_ok & codes_ok & err_ok
+    bad_uncert = ~cert & ~same & ~admissible
+    return {
+        "groups": int(n * ng),
+        "uncertified": int((~cert).sum()),
+        "differ": int((~same).sum()),
+        "bad_certified": int(bad_cert.sum()),
+        "bad_uncertified": int(bad_uncert.sum()),
+        "ok": bool(bad_cert.sum() == 0 and bad_uncert.sum() == 0),
+    }

@@ -1,0 +1,436 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a closed form, a textbook or library
+routine, exact rational arithmetic or an invariant of the method (SquareQ
+README, "SquareQ v3 - W4" section).  ``test_planted_mistakes`` at the end
+plants plausible mistakes in the oracle and shows a pin here catches each.
+"""
+from fractions import Fraction
+import itertools
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+import oracle as O
+from synth import f32_to_bf16_bits, bf16_bits_to_f32
+
+
+# ----------------------------------------------------------------- Hadamard
+def pin_sylvester_matches_kronecker():
+    # textbook recursion S_2n = [[S, S], [S, -S]], independent of popcount
+    s = np.array([[1.0]])
+    while s.shape[0] < 256:
+        s = np.block([[s, s], [s, -s]])
+    assert np.array_equal(O.sylvester(256), s)
+    # and the library's Sylvester construction
+    assert np.array_equal(O.sylvester(256), scipy.linalg.hadamard(256).astype(float))
+
+
+def pin_hadamard_orthonormal_selfinverse():
+    h = O.hadamard256()
+    assert np.array_equal(h, h.T)
+    assert np.array_equal(h @ h, np.eye(256))           # exact: sums of +-1/256
+
+
+def pin_rotate_blocks():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 768))
+    r = O.rotate(x)
+    # block-diagonal: each 256-block transforms on its own, H applied on the right
+    h = scipy.linalg.hadamard(256) / 16.0
+    for b in range(3):
+        np.testing.assert_allclose(r[:, 256 * b:256 * b + 256], x[:, 256 * b:256 * b + 256] @ h,
+                                   rtol=0, atol=1e-13)
+    np.testing.assert_allclose(r, O.fwht_fast(x), rtol=0, atol=1e-13)
+    # self-inverse and Parseval per block
+    np.testing.assert_allclose(O.rotate(r), x, rtol=0, atol=1e-13)
+    np.testing.assert_allclose((r.reshape(5, 3, 256) ** 2).sum(-1),
+                               (x.reshape(5, 3, 256) ** 2).sum(-1), rtol=1e-13)
+    # unit vectors: e0 -> 1/16 * ones ; ones -> 16 * e0
+    e0 = np.zeros((1, 256)); e0[0, 0] = 1
+    assert np.array_equal(O.rotate(e0), np.full((1, 256), 1 / 16))
+    assert np.array_equal(O.rotate(np.ones((1, 256))), 16 * e0)
+    # e_j -> row j of H: sign pattern (-1)^popcount(j & i)
+    ej = np.zeros((1, 256)); ej[0, 37] = 1
+    expect = np.array([(-1) ** bin(37 & i).count("1") for i in range(256)]) / 16
+    assert np.array_equal(O.rotate(ej)[0], expect)
+
+
+# ----------------------------------------------------------------- formats
+def pin_fp16_round_matches_ieee():
+    rng = np.random.default_rng(2)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 5, 20000),
+        # exact ties between neighbours (round to even)
+        (np.arange(1, 2000) * 2 + 1) * 2.0 ** -11 + 1.0,
+        [65504.0, 65519.99, 65520.0, -65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25, 1e-9, 0.0],
+    ])
+    ours = O.fp16_round(v)
+    with np.errstate(over="ignore"):
+        lib = v.astype(np.float16).astype(np.float64)   # numpy rounds fp64 -> fp16 correctly
+    assert np.array_equal(ours, lib, equal_nan=True)
+
+
+def pin_bf16_round_matches_torch():
+    rng = np.random.default_rng(3)
+    v32 = (rng.standard_normal(50000) * 10.0 ** rng.integers(-30, 30, 50000)).astype(np.float32)
+    ties = (1.0 + (np.arange(1, 500) * 2 + 1) * 2.0 ** -8).astype(np.float32)
+    v32 = np.concatenate([v32, ties, -ties])
+    ours = O.bf16_round(v32.astype(np.float64))
+    lib = torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, lib)
+    # the generator's bit encoding agrees too (fp32 inputs)
+    assert np.array_equal(bf16_bits_to_f32(f32_to_bf16_bits(v32)).astype(np.float64), ours)
+
+
+def pin_bf16_no_double_rounding():
+    # x just above a bf16 tie: fp32 would round it onto the tie, fp64 -> bf16 must not
+    x = 1.0 + 2.0 ** -8 + 2.0 ** -40          # tie at 1 + 2^-8 between 1 and 1 + 2^-7
+    assert O.bf16_round(np.array([x]))[0] == 1.0 + 2.0 ** -7
+
+
+# ----------------------------------------------------------------- SVD split
+def pin_svd_split():
+    rng = np.random.default_rng(4)
+    n, k, r = 96, 80, 6
+    u = np.linalg.qr(rng.standard_normal((n, r)))[0]
+    v = np.linalg.qr(rng.standard_normal((k, r)))[0]
+    sig = np.array([9.0, 7, 5, 3, 2, 1])
+    w = (u * sig) @ v.T
+    up, dn = O.svd_init(w, r, round_bf16=False)
+    np.testing.assert_allclose(up @ dn.T, w, atol=1e-12)          # exact at full rank
+    up, dn = O.svd_init(w, 32)                                    # rank > true rank: zero tail
+    assert up.shape == (n, 32) and dn.shape == (k, 32)
+    assert O.rel_fro(up @ dn.T, w) < 8e-3                         # only bf16 rounding left
+    # Eckart-Young on a generic matrix
+    w2 = rng.standard_normal((64, 48))
+    s = np.linalg.svd(w2, compute_uv=False)
+    for rank in (1, 5, 20):
+        up, dn = O.svd_init(w2, rank, round_bf16=False)
+        err = ((w2 - up @ dn.T) ** 2).sum()
+        assert abs(err - (s[rank:] ** 2).sum()) < 1e-9 * (s ** 2).sum()
+    # bf16 factors: every entry is a bf16 value
+    up, dn = O.svd_init(w2, 8)
+    assert np.array_equal(O.bf16_round(up), up) and np.array_equal(O.bf16_round(dn), dn)
+
+
+def pin_spike_recovered():
+    from synth import gen_weight
+    rng = np.random.default_rng(5)
+    w = gen_weight(rng, 512, 512, 4).astype(np.float64)
+    s = np.linalg.svd(w, compute_uv=False)
+    # planted singular values 8..2 dominate the N(0,1/K) bulk (edge ~ 2)
+    np.testing.assert_allclose(s[:3], [8, 6, 4], rtol=0.1)
+
+
+# ----------------------------------------------------------------- sweep
+def _fp16_round_exact(v: Fraction) -> Fraction:
+    """IEEE binary16 RNE of a non-negative rational, in exact arithmetic."""
+    if v == 0:
+        return Fraction(0)
+    e = 0
+    while Fraction(2) ** e > v:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= v:
+        e += 1
+    e = max(e, -14)
+    spacing = Fraction(2) ** (e - 10)
+    n = v / spacing
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    out = fl * spacing
+    assert out <= 65504
+    return out
+
+
+def _rint_half_even(t: Fraction) -> int:
+    fl = t.numerator // t.denominator
+    rem = t - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+def _sweep_exact(r):
+    """Brute-force sweep of one group in exact rational arithmetic."""
+    rf = [Fraction(x) for x in r]
+    a = max(abs(x) for x in rf)
+    best = None
+    for i in range(31):
+        s = _fp16_round_exact(Fraction(70 + i, 700) * a)
+        q = [0 if s == 0 else min(7, max(-8, _rint_half_even(x / s))) for x in rf]
+        e = sum((x - qq * s) ** 2 for x, qq in zip(rf, q))
+        if best is None or e < best[0]:
+            best = (e, i, s, q)
+    return best
+
+
+def pin_sweep_exact_rational():
+    rng = np.random.default_rng(6)
+    groups = []
+    for g in (32, 64):
+        for _ in range(12):
+            # dyadic values so the fp64 oracle's inputs are exact
+            r = rng.integers(-4000, 4001, g) * 2.0 ** -14
+            groups.append(r)
+        # groups whose absmax is negative (the asymmetric -8 side)
+        r = rng.integers(-300, 301, g) * 2.0 ** -12
+        r[3] = -1000 * 2.0 ** -12
+        groups.append(r)
+        # heavy tails
+        r = np.round(rng.standard_t(2, g) * 256) * 2.0 ** -10
+        groups.append(r)
+        # exact half-integer ties at the winning scale (f = 1.00, s = 100 * 2^-10):
+        # values on that grid with large codes plus one or two half-way values,
+        # so the rounding rule decides the emitted codes
+        for _ in range(4):
+            kk = rng.choice([-7, -6, -5, -4, 4, 5, 6, 7], g).astype(float)
+            kk[0] = 7
+            kk[1:3] = rng.choice([-1.5, -0.5, 0.5, 1.5, 2.5], 2)
+            groups.append(kk * 100 * 2.0 ** -10)
+    for r in groups:
+        g = len(r)
+        res = O.quantize_residual(np.tile(r, 256 // g)[None, :], g)
+        e, i, s, q = _sweep_exact(r)
+        assert res.fidx[0, 0] == i
+        assert res.scale[0, 0] == float(s)
+        assert np.array_equal(res.q[0, :g], np.array(q))
+        assert abs(res.mse[0, 0, i] - float(e)) <= 1e-12 * max(float(e), 1e-30)
+
+
+def pin_grid_planted():
+    rng = np.random.default_rng(7)
+    for g in (32, 64):
+        n, k = 8, 512
+        q = rng.integers(-7, 8, (n, k))
+        q[:, ::g] = 7 * rng.choice([-1, 1], (n, k // g))            # |q| = 7 in every group
+        s = O.fp16_round(rng.uniform(1e-3, 3e-2, (n, k // g)))
+        r = q * np.repeat(s, g, axis=1)
+        res = O.quantize_residual(r, g)
+        assert np.array_equal(res.q, q)
+        assert np.array_equal(res.scale, s)
+        assert np.all(res.fidx == 30)
+        best = np.take_along_axis(res.mse, res.fidx[..., None].astype(int), 2)[..., 0]
+        assert np.all(best == 0)
+
+
+def pin_sweep_invariances():
+    rng = np.random.default_rng(8)
+    r = rng.standard_normal((6, 512)) * 0.01
+    base = O.quantize_residual(r, 32)
+    for k in (-3, 4):
+        sc = O.quantize_residual(r * 2.0 ** k, 32)
+        assert np.array_equal(sc.q, base.q) and np.array_equal(sc.fidx, base.fidx)
+        assert np.array_equal(sc.scale, base.scale * 2.0 ** k)
+    # permuting whole groups permutes the result
+    perm = rng.permutation(16)
+    rp = r.reshape(6, 16, 32)[:, perm].reshape(6, 512)
+    pp = O.quantize_residual(rp, 32)
+    assert np.array_equal(pp.fidx, base.fidx[:, perm])
+    assert np.array_equal(pp.q.reshape(6, 16, 32), base.q.reshape(6, 16, 32)[:, perm])
+    # the chosen error never exceeds plain round-to-nearest at f = 1.00
+    best = np.take_along_axis(base.mse, base.fidx[..., None].astype(int), 2)[..., 0]
+    assert np.all(best <= base.mse[..., 30])
+    # all-zero group: scale 0, codes 0, index 0
+    z = r.copy(); z[2, 64:96] = 0
+    zr = O.quantize_residual(z, 32)
+    assert zr.fidx[2, 2] == 0 and zr.scale[2, 2] == 0 and np.all(zr.q[2, 64:96] == 0)
+    # codes stay in range; the -8 code is reachable
+    assert base.q.min() >= -8 and base.q.max() <= 7
+    neg = np.zeros((1, 256)); neg[0, :32] = np.linspace(-1, 0.5, 32) * 0.01
+    assert O.quantize_residual(neg, 32).q.min() == -8
+
+
+def pin_non_finite_raises():
+    r = np.zeros((1, 256)); r[0, 5] = np.nan
+    with pytest.raises(FloatingPointError):
+        O.quantize_residual(r, 32)
+    r = np.zeros((1, 256)); r[0, 5] = 1e6                   # a/7 > 65504
+    with pytest.raises(FloatingPointError):
+        O.quantize_residual(r, 32)
+
+
+# ----------------------------------------------------------------- packing
+def pin_pack():
+    assert list(O.pack(np.array([[1, -1, -8, 7]]))[0]) == [0xF1, 0x78]
+    allbytes = np.arange(256, dtype=np.uint8)[None, :]
+    assert np.array_equal(O.pack(O.unpack(allbytes)), allbytes)
+    q = np.array([[0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1]])
+    assert np.array_equal(O.unpack(O.pack(q)), q)
+
+
+# ----------------------------------------------------------------- the layer
+def _payload(rng, n, k, g, rank):
+    q = rng.integers(-8, 8, (n, k))
+    s = O.fp16_round(rng.uniform(1e-3, 1e-2, (n, k // g)))
+    up = O.bf16_round(rng.standard_normal((n, rank)) * 0.1)
+    dn = O.bf16_round(rng.standard_normal((k, rank)) * 0.1)
+    return q, s, up, dn
+
+
+def pin_reconstruct_roundtrip():
+    rng = np.random.default_rng(9)
+    n, k, g = 16, 512, 32
+    q = rng.integers(-7, 8, (n, k)); q[:, ::g] = 7
+    s = O.fp16_round(rng.uniform(1e-3, 1e-2, (n, k // g)))
+    up = O.bf16_round(rng.standard_normal((n, 32)) * 0.1)
+    dn = O.bf16_round(rng.standard_normal((k, 32)) * 0.1)
+    w = up @ dn.T + O.rotate(q * np.repeat(s, g, 1))      # a weight on the W4 grid
+    res = O.quantize_weight(w, up, dn, g)
+    assert np.array_equal(res.q, q) and np.array_equal(res.scale, s) and np.all(res.fidx == 30)
+    np.testing.assert_allclose(O.reconstruct(res.q, res.scale, up, dn, g), w, rtol=0, atol=1e-15)
+
+
+def pin_forward_consistent():
+    rng = np.random.default_rng(10)
+    n, k, g, m = 24, 512, 64, 7
+    q, s, up, dn = _payload(rng, n, k, g, 32)
+    x = O.bf16_round(rng.standard_normal((m, k)))
+    y = O.forward(x, q, s, up, dn, g)
+    what = O.reconstruct(q, s, up, dn, g)
+    np.testing.assert_allclose(y, x @ what.T, rtol=1e-12, atol=1e-13)
+    # linearity in x
+    x2 = O.bf16_round(rng.standard_normal((m, k)))
+    np.testing.assert_allclose(O.forward(x + 2 * x2, q, s, up, dn, g),
+                               y + 2 * O.forward(x2, q, s, up, dn, g), atol=1e-12)
+    # rank 0: a rotated int4 GEMM
+    y0 = O.forward(x, q, s, up[:, :0], dn[:, :0], g)
+    d = q * np.repeat(s, g, 1)
+    np.testing.assert_allclose(y0, x @ O.rotate(d).T, atol=1e-12)
+    # diagnostic fp16-operand forward: equal when every operand is fp16-exact
+    xi = rng.integers(-3, 4, (m, k)).astype(float) * 16     # rotate(x) lands on small integers/16
+    qi = rng.integers(-8, 8, (n, k)); si = np.full((n, k // g), 2.0 ** -7)
+    np.testing.assert_allclose(O.forward_fp16_operands(xi, qi, si, up, dn, g),
+                               O.forward(xi, qi, si, up, dn, g), rtol=1e-12, atol=1e-12)
+    # and close (fp16 rounding) in general, also with large activations
+    yd = O.forward_fp16_operands(x * 3000, q, s, up, dn, g)
+    assert np.all(np.isfinite(yd))
+    assert O.rel_fro(yd, O.forward(x * 3000, q, s, up, dn, g)) < 2e-3
+
+
+def pin_low_rank_weight():
+    rng = np.random.default_rng(11)
+    n, k = 128, 512
+    u = np.linalg.qr(rng.standard_normal((n, 8)))[0]
+    v = np.linalg.qr(rng.standard_normal((k, 8)))[0]
+    w = (u * np.linspace(8, 2, 8)) @ v.T
+    up, dn = O.svd_init(w, 32)
+    r = O.residual(w, up, dn)
+    assert np.linalg.norm(r) < 1e-2 * np.linalg.norm(w)       # only bf16 rounding remains
+
+
+def pin_group_granularity():
+    # finer groups fit better on average (a statistical, not per-instance, property)
+    rng = np.random.default_rng(12)
+    r = rng.standard_normal((64, 1024)) / 32
+    e = {}
+    for g in (32, 64):
+        res = O.quantize_residual(r, g)
+        e[g] = O.rel_fro(O.dequant(res.q, res.scale, g), r)
+    assert e[32] < e[64] < 0.2
+
+
+def pin_certification():
+    rng = np.random.default_rng(13)
+    r = rng.standard_normal((32, 512)) * 0.01
+    res = O.quantize_residual(r, 32)
+    rep = O.check_device_quant(r, res, 32, res.q, res.scale, res.fidx)
+    assert rep["ok"] and rep["differ"] == 0
+    cert = O.certify(r, res, 32)
+    assert cert.mean() > 0.8
+    # flipping a code in a certified group is caught
+    gi = np.argwhere(cert)[0]
+    qd = res.q.copy()
+    qd[gi[0], gi[1] * 32] = (qd[gi[0], gi[1] * 32] + 1) if qd[gi[0], gi[1] * 32] < 7 else 6
+    assert not O.check_device_quant(r, res, 32, qd, res.scale, res.fidx)["ok"]
+    # a wrong index with its own consistent scale/codes is caught too
+    fd = res.fidx.copy(); fd[gi[0], gi[1]] = (fd[gi[0], gi[1]] + 5) % 31
+    sd = res.scale.copy()
+    sd[gi[0], gi[1]] = O.fp16_round(O.candidate_scale_exact(res.absmax[gi[0], gi[1]], fd[gi[0], gi[1]]))
+    qd = res.q.copy()
+    seg = slice(gi[1] * 32, gi[1] * 32 + 32)
+    qd[gi[0], seg] = O.codes_for_scale(r[gi[0], seg], sd[gi[0], gi[1]])
+    assert not O.check_device_quant(r, res, 32, qd, sd, fd)["ok"]
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    pin()
+
+
+# ----------------------------------------------------------------- planted mistakes
+def _mutations():
+    """Plausible mistakes, each planted in the oracle on the CPU."""
+    orig_h = O.sq_oracle.hadamard256
+    orig_codes = O.sq_oracle.codes_for_scale
+    orig_dequant = O.sq_oracle.dequant
+    orig_fwd = O.sq_oracle.forward
+    orig_pack = O.sq_oracle.pack
+    orig_scale = O.sq_oracle.candidate_scale_exact
+    orig_svd = O.sq_oracle.svd_init
+
+    def unnormalised():
+        return orig_h() * 16
+
+    def half_away(r, s):
+        r = np.asarray(r, float); s = np.asarray(s, float)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            t = r / s
+            q = np.clip(np.sign(t) * np.floor(np.abs(t) + 0.5), -8, 7)
+        return np.where(s == 0, 0.0, q)
+
+    def symmetric_clamp(r, s):
+        return np.clip(orig_codes(r, s), -7, 7)
+
+    def tiled_groups(q, scale, group):
+        q = np.asarray(q, float)
+        return q * np.tile(np.asarray(scale, float), group)
+
+    def dropped_lowrank(x, q, scale, up, down, group):
+        return orig_fwd(x, q, scale, up[:, :0], down[:, :0], group)
+
+    def swapped_nibbles(q):
+        q = np.asarray(q).astype(np.int64)
+        return ((q[..., 1::2] & 0xF) | ((q[..., 0::2] & 0xF) << 4)).astype(np.uint8)
+
+    def fraction_off_by_one(a, i):
+        return orig_scale(a, np.asarray(i) + 1)
+
+    def svd_no_sqrt(w, rank=32, round_bf16=True):
+        w = np.asarray(w, float)
+        u, s, vt = np.linalg.svd(w, full_matrices=False)
+        up, dn = u[:, :rank] * s[:rank], vt[:rank].T * s[:rank]
+        return (O.bf16_round(up), O.bf16_round(dn)) if round_bf16 else (up, dn)
+
+    return [
+        ("hadamard256", unnormalised),
+        ("codes_for_scale", half_away),
+        ("codes_for_scale", symmetric_clamp),
+        ("dequant", tiled_groups),
+        ("forward", dropped_lowrank),
+        ("pack", swapped_nibbles),
+        ("candidate_scale_exact", fraction_off_by_one),
+        ("svd_init", svd_no_sqrt),
+    ]
+
+
+@pytest.mark.parametrize("name,mutant", _mutations(), ids=lambda v: getattr(v, "__name__", str(v)))
+def test_planted_mistakes(monkeypatch, name, mutant):
+    monkeypatch.setattr(O.sq_oracle, name, mutant)
+    monkeypatch.setattr(O, name, mutant, raising=False)
+    if name == "hadamard256":
+        monkeypatch.setattr(O.sq_oracle, "_H", None)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception:
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake in {name}"
