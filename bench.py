@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Throughput of the W4 linear layer's hot path on one MI355X.
+
+One step = the three entry points on one synthetic layer with the inputs
+already resident in HBM:
+  sq_quantize_weight (rotate + MSE fraction sweep + int4 pack of W),
+  sq_linear_fwd      (rotation pre-phase + fused int4 contraction),
+  sq_reconstruct_bf16 (bf16 W_hat from the payload).
+Each entry point is timed on its own with HIP events on the stream it runs
+on (torch's current stream), after warm-up calls; the reconstruct rotates
+over three payload/output sets so the 256 MB Infinity Cache cannot serve its
+reads.  The headline `value` is the fused forward's TFLOP/s at
+4480x16384x6144 (flops = 2MNK + 2Mr(N+K)); reconstruct GB/s and quantize
+GB/s are reported beside it.
+
+The `roofline` object is for the forward's dominant kernel (the contraction,
+k_fwd_gemm, timed alone through sq_linear_fwd_contract).  `cpu_baseline` is
+the CPU oracle's forward on a sample of rows, on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 4]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--ops", default="fwd,reconstruct,quantize")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; the layer shards by output rows "
+              "(see the design notes), but no multi-GPU measurement exists.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import w4_gemm_amd as W
+    from synth import CONFIGS, f32_to_bf16_bits, gen_activations, gen_weight
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.config]
+    M, N, K, G, R = cfg.M, cfg.N, cfg.K, cfg.group, cfg.rank
+    ops = args.ops.split(",")
+
+    # ---------------------------------------------------------------- inputs (untimed)
+    t_setup = time.time()
+    rng = np.random.default_rng(0)
+    w_np = gen_weight(rng, N, K, cfg.spike)
+    x_np = gen_activations(rng, M, K, cfg.outlier_frac)
+    w = torch.from_numpy(w_np).to(dev)
+    x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
+    del w_np
+    # host prerequisite: rank-R factors.  A randomized range finder stands in for
+    # the full fp64 SVD here (same shapes and magnitudes; kernel cost does not
+    # depend on the factor values).
+    torch.manual_seed(0)
+    u, s, v = torch.svd_lowrank(w, q=R + 8, niter=2)
+    rs = s[:R].sqrt()
+    up = (u[:, :R] * rs).to(torch.bfloat16).contiguous()
+    down = (v[:, :R] * rs).to(torch.bfloat16).contiguous()
+    del u, s, v
+    p0, fidx, flags = W.quantize_weight(w, up, down, G)
+    torch.cuda.synchronize()
+    assert int(flags[0]) == 0, "quantizer flagged the synthetic weight"
+    payloads = [p0] + [W.W4Payload(p0.codes.clone(), p0.scales.clone(), up, down, G) for _ in range(2)]
+    ws = torch.empty(W.fwd_workspace_bytes(M, p0), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    what = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    res = {}
+    torch.cuda.synchronize()
+    t0 = time.time()
+    # ---------------------------------------------------------------- forward
+    if "fwd" in ops:
+        for _ in range(args.warmup):
+            W.linear_fwd_rotate(x, p0, ws)
+            W.linear_fwd_contract(M, p0, y, ws)
+        marks = [(ev(), ev(), ev()) for _ in range(args.steps)]
+        for a, b, c in marks:
+            a.record()
+            W.linear_fwd_rotate(x, p0, ws)
+            b.record()
+            W.linear_fwd_contract(M, p0, y, ws)
+            c.record()
+        torch.cuda.synchronize()
+        rot = np.array([a.elapsed_time(b) for a, b, _ in marks])
+        con = np.array([b.elapsed_time(c) for _, b, c in marks])
+        res["fwd"] = (rot + con, rot, con)
+    # ---------------------------------------------------------------- reconstruct
+    if "reconstruct" in ops:
+        for i in range(args.warmup):
+            W.reconstruct_bf16(payloads[i % 3], out=what[i % 3])
+        marks = [(ev(), ev()) for _ in range(args.steps)]
+        for i, (a, b) in enumerate(marks):
+            a.record()
+            W.reconstruct_bf16(payloads[i % 3], out=what[i % 3])
+            b.record()
+        torch.cuda.synchronize()
+        res["reconstruct"] = np.array([a.elapsed_time(b) for a, b in marks])
+    # ---------------------------------------------------------------- quantize
+    if "quantize" in ops:
+        qp = W.empty_payload(N, K, G, R, dev)
+        qp.up, qp.down = up, down
+        qf = torch.empty((N, K // G), dtype=torch.uint8, device=dev)
+        qflags = torch.zeros(4, dtype=torch.int32, device=dev)
+        from w4_gemm_amd import _lib
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def quant():
+            st = _lib.sq_quantize_weight(w.data_ptr(), qp.abi(), qf.data_ptr(), qflags.data_ptr(), stream)
+            assert st == 0, st
+        for _ in range(args.warmup):
+            quant()
+        marks = [(ev(), ev()) for _ in range(args.steps)]
+        for a, b in marks:
+            a.record()
+            quant()
+            b.record()
+        torch.cuda.synchronize()
+        res["quantize"] = np.array([a.elapsed_time(b) for a, b in marks])
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+
+    # ---------------------------------------------------------------- metrics
+    flops_fwd = 2.0 * M * N * K + 2.0 * M * R * (N + K)
+    flops_gemm = 2.0 * M * N * K + 2.0 * M * N * R
+    pay_bytes = N * K / 2 + N * (K // G) * 2 + (N + K) * R * 2
+    rec_bytes = pay_bytes + 2.0 * N * K
+    quant_bytes = 4.0 * N * K + N * K / 2 + N * (K // G) * 3 + (N + K) * R * 2
+    out = {}
+    ms_step = 0.0
+    if "fwd" in res:
+        tot, rot, con = res["fwd"]
+        t_fwd, t_rot, t_con = float(np.mean(tot)), float(np.mean(rot)), float(np.mean(con))
+        ms_step += t_fwd
+        out.update(fwd_ms=t_fwd, fwd_ms_p10=float(np.percentile(tot, 10)),
+                   fwd_ms_p90=float(np.percentile(tot, 90)), fwd_rotate_ms=t_rot,
+                   fwd_contract_ms=t_con, fwd_tflops=flops_fwd / (t_fwd * 1e-3) / 1e12)
+        out["fwd_pct_bf16_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_F16_TFLOPS
+        achieved = flops_gemm / (t_con * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": "k_fwd_gemm", "achieved": achieved,
+                           "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": achieved / PEAK_F16_TFLOPS, "traffic": None,
+                           "per_launch_flops": flops_gemm}
+    if "reconstruct" in res:
+        t = float(np.mean(res["reconstruct"]))
+        ms_step += t
+        out.update(reconstruct_ms=t, reconstruct_gbps=rec_bytes / (t * 1e-3) / 1e9)
+        out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
+    if "quantize" in res:
+        t = float(np.mean(res["quantize"]))
+        ms_step += t
+        out.update(quantize_ms=t, quantize_gbps=quant_bytes / (t * 1e-3) / 1e9)
+        out["quantize_pct_hbm_peak"] = 100.0 * out["quantize_gbps"] / PEAK_HBM_GBPS
+
+    line = {
+        "metric": "fused W4 fwd TFLOP/s (% bf16 MFMA peak) at 4480x16384x6144; reconstruct GB/s",
+        "value": out.get("fwd_tflops"),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} rank{R}", "M": M, "N": N, "K": K, "group": G,
+                   "rank": R, "out_dtype": "bf16"},
+        "roofline": out.pop("roofline", None),
+        "cpu_baseline": None,
+    }
+    line.update({k: v for k, v in out.items()})
+    line["timed_wall_s"] = wall
+    line["setup_s"] = t_setup
+    line["device"] = torch.cuda.get_device_name(0)
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(p0, x, cfg, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(p, x, cfg, rows):
+    """The oracle's forward on `rows` sampled rows of x against the full payload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    codes = p.codes.cpu().numpy()
+    scales = p.scales.cpu().numpy()
+    up = p.up.float().cpu().numpy().astype(np.float64)
+    dn = p.down.float().cpu().numpy().astype(np.float64)
+    sel = np.sort(np.random.default_rng(1).choice(cfg.M, rows, replace=False))
+    xs = x[sel].float().cpu().numpy().astype(np.float64)
+    t = time.perf_counter()
+    q = O.unpack(codes)
+    y = O.forward(xs, q, O.fp16_decode(scales), up, dn, cfg.group)
+    dt = time.perf_counter() - t
+    assert np.all(np.isfinite(y))
+    flops = 2.0 * rows * cfg.N * cfg.K + 2.0 * rows * cfg.rank * (cfg.N + cfg.K)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle.forward (numpy fp64) on {rows} of {cfg.M} rows, full N={cfg.N} "
+                      f"K={cfg.K}, including unpack/dequant; {dt:.2f} s",
+            "seconds": dt}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

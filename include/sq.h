@@ -1,0 +1,135 @@
+/* sq.h - C ABI of libsq, the MI355X (gfx950) W4 quantized-frozen-base linear layer.
+ *
+ * The layer is the SquareQ v3 W4 format (SquareQ README, section "SquareQ v3 -
+ * W4 (Hadamard-256 + low-rank + int4 / NVFP4)", the format formula and its
+ * "Rotation", "Residual codecs" and "Low-rank branch" bullets):
+ *
+ *     W_hat = lora_up @ lora_down^T + dequant(R) @ H
+ *
+ * H is the block-diagonal normalized Hadamard-256 rotation along the input
+ * dimension K (Sylvester order, entries +-1/16, symmetric and its own inverse),
+ * R holds int4 codes with one fp16 scale per group of 32 or 64 consecutive
+ * values along K, and lora_up / lora_down are the bf16 rank-r factors of an
+ * SVD of the weight.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no device memory and keeps no state besides a per-device
+ *     architecture check.  Calls are reentrant.
+ *   - Arguments are validated synchronously on the host; on any error nothing
+ *     is launched and the status says why.  Kernel work is enqueued on
+ *     `stream` (a hipStream_t; NULL means the null stream) and is asynchronous:
+ *     the library never synchronizes.
+ *   - There is exactly one device code path per call and no host fallback: a
+ *     device that is not gfx950 gets SQ_E_ARCH.
+ *   - All tensors are dense and row-major; every pointer must be 16-byte
+ *     aligned (SQ_E_ALIGN).
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SQ_ABI_VERSION 1
+
+typedef enum {
+  SQ_OK = 0,
+  SQ_E_NULL = 1,      /* a required pointer is NULL                               */
+  SQ_E_SHAPE = 2,     /* K % 256 != 0, K < 256, N < 1 or M < 0                    */
+  SQ_E_GROUP = 3,     /* group is not 32 or 64                                    */
+  SQ_E_RANK = 4,      /* rank is not 0, 32 or 64                                  */
+  SQ_E_ALIGN = 5,     /* a pointer is not 16-byte aligned                         */
+  SQ_E_WORKSPACE = 6, /* workspace smaller than sq_linear_fwd_workspace_bytes()   */
+  SQ_E_DTYPE = 7,     /* output dtype is not SQ_F32 or SQ_BF16                    */
+  SQ_E_ARCH = 8,      /* the current device is not gfx950                         */
+  SQ_E_HIP = 9        /* a HIP runtime call or kernel launch failed               */
+} sq_status_t;
+
+typedef enum { SQ_F32 = 0, SQ_BF16 = 1 } sq_dtype_t;
+
+/* Bits OR-ed into *dev_flags by the quantizer (read them after a sync). */
+enum {
+  SQ_FLAG_NONFINITE = 1,      /* a weight value, or the residual, is NaN or +-inf      */
+  SQ_FLAG_SCALE_OVERFLOW = 2  /* absmax/7 of some group overflows fp16                 */
+};
+
+/* The W4 payload of one linear layer with N output and K input features.
+ *   codes     uint8  [n][k/2]  byte b of a row = (q[2b] & 0xF) | (q[2b+1] & 0xF) << 4,
+ *                              q in [-8, 7] two's complement (even k in the low nibble)
+ *   scales    fp16   [n][k/group]  IEEE binary16 bit patterns
+ *   lora_up   bf16   [n][rank]     (may be NULL iff rank == 0)
+ *   lora_down bf16   [k][rank]     (may be NULL iff rank == 0)
+ * Scale g of row n covers q[n][g*group .. g*group+group-1]; those values are
+ * coordinates after the rotation, so dequant(R)[n][k] = q[n][k] * s[n][k/group]. */
+typedef struct {
+  int64_t n, k;
+  int32_t group, rank;
+  uint8_t *codes;
+  uint16_t *scales;
+  uint16_t *lora_up;
+  uint16_t *lora_down;
+} sq_w4_t;
+
+/* Builder side (the format formula read right to left, the "Residual codecs"
+ * bullet): quantize the fp32 weight w [n][k].
+ *   E = w - lora_up @ lora_down^T           (fp32; the factors are read from p)
+ *   R = E @ H                                (block Hadamard-256 along k)
+ *   for every group of `group` values of R with absmax a and every
+ *   i = 0..30: s_i = fp16(round((70+i)/100 * a / 7)),
+ *   q = clamp(round_half_even(r / s_i), -8, 7) (q = 0 when s_i == 0),
+ *   err_i = sum (r - q s_i)^2; the first i with the least err wins.
+ * Writes p->codes, p->scales and, when fidx != NULL, fidx[n][k/group] = i
+ * (uint8).  Non-finite inputs and fp16 scale overflow set bits in *dev_flags
+ * (device int32, required; the library only ORs bits into it, so clear it
+ * first); outputs are then unspecified but written in bounds. */
+sq_status_t sq_quantize_weight(const float *w, const sq_w4_t *p, uint8_t *fidx,
+                               int32_t *dev_flags, void *stream);
+
+/* Forward (the format formula applied to x; H is symmetric so
+ * x @ (dequant(R) @ H)^T = (x @ H) @ dequant(R)^T):
+ *   y[m][n] = sum_k (x @ H)[m][k] * q[n][k] * s[n][k/group]
+ *           + sum_r (x @ lora_down)[m][r] * lora_up[n][r]
+ * x is bf16 [m][k]; y is fp32 or bf16 [m][n] (bf16 = round-to-nearest-even of
+ * the fp32 result).  The contraction runs on fp16 MFMA: each row of x @ H is
+ * scaled by a power of two that keeps it inside fp16 range and rounded to
+ * fp16, the weight operand is fp16(q * s); accumulation is fp32.
+ * `workspace` is device scratch of at least sq_linear_fwd_workspace_bytes(m, p)
+ * bytes, owned by the caller and not read before it is written.  m == 0 is a
+ * no-op that returns SQ_OK. */
+size_t sq_linear_fwd_workspace_bytes(int64_t m, const sq_w4_t *p);
+sq_status_t sq_linear_fwd(const uint16_t *x, int64_t m, const sq_w4_t *p, void *y,
+                          sq_dtype_t y_dtype, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* The same forward in its two halves; sq_linear_fwd is exactly
+ * sq_linear_fwd_rotate followed by sq_linear_fwd_contract on one stream.
+ *   rotate:   reads x, p->lora_down; writes into `workspace` the fp16 rotated
+ *             activations, the row powers of two and the rank-r projection
+ *             x @ lora_down.
+ *   contract: reads that workspace and the payload; writes y.
+ * Both take the same m, p and workspace; contract must follow a rotate of the
+ * same x on the same workspace (stream order suffices). */
+sq_status_t sq_linear_fwd_rotate(const uint16_t *x, int64_t m, const sq_w4_t *p, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+sq_status_t sq_linear_fwd_contract(int64_t m, const sq_w4_t *p, void *y, sq_dtype_t y_dtype,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Backward side: rebuild the dense bf16 weight from the same payload
+ *   w_hat[n][k] = bf16_round_nearest_even( lora_up @ lora_down^T + dequant(R) @ H )
+ * with every intermediate in fp32 and one rounding at the end. */
+sq_status_t sq_reconstruct_bf16(const sq_w4_t *p, uint16_t *w_hat, void *stream);
+
+/* Static description of a status code; never NULL. */
+const char *sq_status_str(sq_status_t status);
+int sq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

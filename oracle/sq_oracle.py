@@ -372,6 +372,30 @@ def _fp16_boundary_margin(v) -> np.ndarray:
     return out
 
 
+def _variant_mse(rg, a):
+    """Error of every candidate under each admissible fp16 rounding of its scale.
+
+    Returns (scales [.., 31, 2], mse [.., 31, 2]): variant 0 is the correct
+    rounding; variant 1 is the other fp16 neighbour when the unrounded scale
+    lies within SCALE_MARGIN of a rounding boundary, else a copy of variant 0.
+    A device that computes the absmax in fp32 may take either variant there.
+    """
+    shape = a.shape + (N_FRAC, 2)
+    sc = np.empty(shape)
+    ms = np.empty(shape)
+    for i in range(N_FRAC):
+        v = candidate_scale_exact(a, i)
+        s0 = fp16_round(v)
+        lo, hi = _fp16_bracket(v)
+        amb = _fp16_boundary_margin(v) <= SCALE_MARGIN
+        s1 = np.where(amb, np.where(s0 == lo, hi, lo), s0)
+        for j, sv in enumerate((s0, s1)):
+            q = codes_for_scale(rg, sv[..., None])
+            sc[..., i, j] = sv
+            ms[..., i, j] = ((rg - q * sv[..., None]) ** 2).sum(axis=-1)
+    return sc, ms
+
+
 def certify(r, res: QuantResult, group: int):
     """Per-group flag: True where the oracle's choice is far from every tie.
 
@@ -388,8 +412,7 @@ def certify(r, res: QuantResult, group: int):
     rg = r.reshape(n, k // group, group)
     a = res.absmax
     best = res.fidx.astype(np.int64)
-    v_best = candidate_scale_exact(a, best)
-    ok = _fp16_boundary_margin(v_best) > SCALE_MARGIN
+    ok = _fp16_boundary_margin(candidate_scale_exact(a, best)) > SCALE_MARGIN
     ok |= (a == 0)
     s = res.scale[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
@@ -397,23 +420,11 @@ def certify(r, res: QuantResult, group: int):
     frac = np.abs(t - np.floor(t) - 0.5)
     near = (frac < CODE_MARGIN) & (t > QMIN - 1) & (t < QMAX + 1)
     ok &= ~near.any(axis=2)
-    # sweep margin, including the alternative rounding of ambiguous scales
-    mse_min_other = np.full(a.shape, np.inf)
-    for i in range(N_FRAC):
-        v = candidate_scale_exact(a, i)
-        variants = [fp16_round(v)]
-        amb = _fp16_boundary_margin(v) <= SCALE_MARGIN
-        if np.any(amb):
-            lo, hi = _fp16_bracket(v)
-            variants.append(np.where(amb, lo, variants[0]))
-            variants.append(np.where(amb, hi, variants[0]))
-        for sv in variants:
-            q = codes_for_scale(rg, sv[..., None])
-            m = ((rg - q * sv[..., None]) ** 2).sum(axis=2)
-            is_best = (best == i) & (sv == res.scale)
-            mse_min_other = np.where(is_best, mse_min_other, np.minimum(mse_min_other, m))
+    _, ms = _variant_mse(rg, a)
+    others = ms.min(axis=-1)
+    np.put_along_axis(others, best[..., None], np.inf, axis=2)
     mse_best = np.take_along_axis(res.mse, best[..., None], axis=2)[..., 0]
-    gap_ok = mse_min_other > mse_best * (1 + SWEEP_MARGIN)
+    gap_ok = others.min(axis=2) > mse_best * (1 + SWEEP_MARGIN)
     gap_ok |= (a == 0)
     return ok & gap_ok
 
@@ -422,11 +433,14 @@ def check_device_quant(r, res: QuantResult, group: int, q_dev, scale_dev, fidx_d
     """Compare a device quantization with the oracle under tie certification.
 
     Returns a dict with counts; ``ok`` is True when certified groups match
-    bit for bit and every uncertified group is an admissible near-tie:
-    its scale is one of the two fp16 neighbours of f_j a/7 for the device's
-    index j, its codes are the requantization with that scale except for
-    values within CODE_MARGIN of a half-integer (which may take either
-    neighbour), and its error is within SWEEP_MARGIN of the best.
+    bit for bit and every other differing group is an admissible near-tie:
+      * its scale is an admissible fp16 rounding of f_j a/7 for the device's
+        index j (the correct one, or the other neighbour within SCALE_MARGIN);
+      * its codes are the requantization with that scale, except values within
+        CODE_MARGIN of a half-integer, which may take either neighbour;
+      * its error is at most (1 + SWEEP_MARGIN) times the error of every other
+        candidate i under the rounding of s_i least favourable to i, i.e. some
+        admissible set of roundings makes the device's choice a minimiser.
     """
     r = np.asarray(r, np.float64)
     n, k = r.shape
@@ -439,23 +453,22 @@ def check_device_quant(r, res: QuantResult, group: int, q_dev, scale_dev, fidx_d
     fd = np.asarray(fidx_dev).astype(np.int64)
     same = (fd == res.fidx) & (sd == res.scale) & (qd == qo).all(axis=2)
     bad_cert = cert & ~same
-    # admissibility of every group that differs
-    v = candidate_scale_exact(res.absmax, fd)
-    lo, hi = _fp16_bracket(v)
-    scale_ok = (sd == lo) | (sd == hi)
-    scale_ok |= (res.absmax == 0) & (sd == 0)
+    sc, ms = _variant_mse(rg, res.absmax)
+    cand = np.take_along_axis(sc, np.clip(fd, 0, N_FRAC - 1)[..., None, None], axis=2)[..., 0, :]
+    scale_ok = (sd == cand[..., 0]) | (sd == cand[..., 1])
     with np.errstate(divide="ignore", invalid="ignore"):
         t = np.where(sd[..., None] > 0, rg / np.where(sd[..., None] > 0, sd[..., None], 1), 0.0)
     q_req = np.clip(np.rint(t), QMIN, QMAX)
-    frac = np.abs(t - np.floor(t) - 0.5)
-    near = frac < CODE_MARGIN
+    near = np.abs(t - np.floor(t) - 0.5) < CODE_MARGIN
     q_lo = np.clip(np.floor(t), QMIN, QMAX)
     q_hi = np.clip(np.ceil(t), QMIN, QMAX)
     codes_ok = ((qd == q_req) | (near & ((qd == q_lo) | (qd == q_hi)))).all(axis=2)
     mse_dev = ((rg - qd * sd[..., None]) ** 2).sum(axis=2)
-    mse_best = np.take_along_axis(res.mse, res.fidx[..., None].astype(np.int64), axis=2)[..., 0]
-    err_ok = mse_dev <= mse_best * (1 + SWEEP_MARGIN) + 1e-300
-    admissible = scale_ok & codes_ok & err_ok
+    worst = ms.max(axis=-1)
+    np.put_along_axis(worst, np.clip(fd, 0, N_FRAC - 1)[..., None], np.inf, axis=2)
+    err_ok = mse_dev <= worst.min(axis=2) * (1 + SWEEP_MARGIN)
+    err_ok |= (res.absmax == 0) & (mse_dev == 0)
+    admissible = scale_ok & codes_ok & err_ok & (fd >= 0) & (fd < N_FRAC)
     bad_uncert = ~cert & ~same & ~admissible
     return {
         "groups": int(n * ng),

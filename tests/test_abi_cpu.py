@@ -1,0 +1,85 @@
+"""Host-side checks of libsq that need no GPU: the library loads, exports every
+symbol include/sq.h declares, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4_gemm_amd import _lib
+from w4_gemm_amd._lib import SqW4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "sq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    L = _lib.lib()
+    for name in names:
+        assert hasattr(L, name), name
+    # and they are real dynamic symbols of libsq.so
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in names:
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_version_and_status_strings():
+    assert _lib.abi_version() == 1
+    for s in range(10):
+        assert _lib.status_str(s)
+    assert "unknown" in _lib.status_str(99)
+
+
+def _payload(n=16, k=256, group=32, rank=32, codes=0x1000, scales=0x2000, up=0x3000, down=0x4000):
+    return SqW4(n, k, group, rank, codes, scales, up, down)
+
+
+BAD = [
+    ("k not multiple of 256", dict(k=300), 2),
+    ("k too small", dict(k=0), 2),
+    ("n < 1", dict(n=0), 2),
+    ("group 16", dict(group=16), 3),
+    ("rank 16", dict(rank=16), 4),
+    ("null codes", dict(codes=None), 1),
+    ("null up with rank", dict(up=None), 1),
+    ("misaligned scales", dict(scales=0x2002), 5),
+]
+
+
+@pytest.mark.parametrize("why,kw,status", BAD, ids=[b[0] for b in BAD])
+def test_validation_before_launch(why, kw, status):
+    p = _payload(**kw)
+    assert _lib.sq_reconstruct_bf16(p, 0x5000, None) == status
+    assert _lib.sq_quantize_weight(0x6000, p, None, 0x7000, None) == status
+    assert _lib.sq_linear_fwd(0x8000, 4, p, 0x9000, 0, 0xA000, 1 << 30, None) == status
+
+
+def test_other_arguments():
+    p = _payload()
+    assert _lib.sq_reconstruct_bf16(p, None, None) == 1
+    assert _lib.sq_reconstruct_bf16(p, 0x5008, None) == 5
+    assert _lib.sq_quantize_weight(None, p, None, 0x7000, None) == 1
+    assert _lib.sq_quantize_weight(0x6000, p, None, None, None) == 1
+    assert _lib.sq_linear_fwd(0x8000, -1, p, 0x9000, 0, 0xA000, 1 << 30, None) == 2
+    assert _lib.sq_linear_fwd(0x8000, 4, p, 0x9000, 7, 0xA000, 1 << 30, None) == 7
+    assert _lib.sq_linear_fwd(0x8000, 0, p, 0x9000, 0, None, 0, None) == 0   # m == 0: no-op
+    ws = _lib.sq_linear_fwd_workspace_bytes(4, p)
+    assert _lib.sq_linear_fwd(0x8000, 4, p, 0x9000, 0, 0xA000, ws - 1, None) == 6
+    # rank 0 needs no factors
+    p0 = _payload(rank=0, up=None, down=None)
+    assert _lib.sq_linear_fwd_workspace_bytes(4, p0) > 0
+
+
+def test_workspace_size_grows_with_m():
+    p = _payload(n=3072, k=3072)
+    sizes = [_lib.sq_linear_fwd_workspace_bytes(m, p) for m in (1, 64, 1536)]
+    assert sizes[0] > 0 and sizes[0] <= sizes[1] <= sizes[2]
+    assert sizes[2] >= 1536 * 3072 * 2                 # holds the rotated activations
+    assert _lib.sq_linear_fwd_workspace_bytes(0, p) == 0

@@ -1,0 +1,259 @@
+"""Device parity: libsq's HIP kernels against the CPU oracle.
+
+Bars (from the layer's accuracy contract):
+  * quantize: codes, fp16 scales and fraction indices bit-exact on every
+    tie-certified group; uncertified groups must be admissible near-ties;
+  * reconstruct: bf16 W_hat within 1e-3 relative Frobenius of the oracle's
+    exact W_hat rounded to bf16, and at most 1 bf16 ulp per element;
+  * forward: fp32 y within 2e-3 relative Frobenius (cos >= 0.9999) of the
+    exact fp64 y; within 1e-5 of the oracle evaluated on the same fp16
+    operands; bf16 y is bit-equal to round-to-nearest-even of the fp32 y.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from synth import CONFIGS, gen_layer, gen_payload
+from tests.helpers import (bf16_bits_of, bf16_tensor_to_f64, dev, oracle_payload, payload_fp64,
+                           to_dev_payload, ulp_bf16)
+
+pytestmark = pytest.mark.gpu
+
+Y_TOL, COS_TOL, DIAG_TOL, WHAT_TOL = 2e-3, 0.9999, 1e-5, 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import w4_gemm_amd  # noqa: F401  (fails loudly if libsq.so is missing)
+
+
+def _x_dev(xbits):
+    return torch.from_numpy(xbits.view(np.int16)).view(torch.bfloat16).to(dev())
+
+
+# ------------------------------------------------------------------ config 1, end to end
+@pytest.fixture(scope="module")
+def tiny():
+    cfg, w, xbits = gen_layer(1, seed=0)
+    codes, scales, upb, dnb, res, r, up, dn = oracle_payload(w, cfg.rank, cfg.group)
+    return dict(cfg=cfg, w=w, xbits=xbits, codes=codes, scales=scales, upb=upb, dnb=dnb, res=res,
+                r=r, up=up, dn=dn)
+
+
+def _check_quant(w, up_bits, dn_bits, group, up, dn, tag):
+    import w4_gemm_amd as W
+    d = dev()
+    wt = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(d)
+    upt = torch.from_numpy(up_bits.view(np.int16)).view(torch.bfloat16).to(d) if up_bits is not None else None
+    dnt = torch.from_numpy(dn_bits.view(np.int16)).view(torch.bfloat16).to(d) if dn_bits is not None else None
+    p, fidx, flags = W.quantize_weight(wt, upt, dnt, group)
+    torch.cuda.synchronize()
+    assert int(flags[0]) == 0
+    r = O.residual(w, up, dn)
+    res = O.quantize_residual(r, group)
+    rep = O.check_device_quant(r, res, group, O.unpack(p.codes.cpu().numpy()),
+                               p.scales.cpu().numpy().astype(np.float64), fidx.cpu().numpy())
+    print(tag, rep)
+    assert rep["ok"], rep
+    return rep
+
+
+def test_quantize_tiny(tiny):
+    t = tiny
+    _check_quant(t["w"], t["upb"], t["dnb"], 32, t["up"], t["dn"], "cfg1")
+
+
+def test_quantize_tiny_g64_rank0_ragged():
+    rng = np.random.default_rng(3)
+    from synth import gen_weight
+    w = gen_weight(rng, 100, 768, 4)            # N not a multiple of 16, three blocks
+    up, dn = O.svd_init(w, 32)
+    _check_quant(w, bf16_bits_of(up), bf16_bits_of(dn), 64, up, dn, "ragged g64")
+    _check_quant(w, None, None, 32, np.zeros((100, 0)), np.zeros((768, 0)), "rank0 g32")
+
+
+def test_quantize_edge_groups():
+    # all-zero groups, grid-planted groups (exact), a negative-heavy group
+    import w4_gemm_amd as W
+    rng = np.random.default_rng(4)
+    n, k, g = 16, 512, 32
+    q = rng.integers(-7, 8, (n, k)); q[:, ::g] = 7
+    s = O.fp16_round(rng.uniform(1e-3, 1e-2, (n, k // g)))
+    r_plant = q * np.repeat(s, g, 1)
+    w = O.rotate(r_plant)                                  # rank 0: W = R H
+    w[3, :] = 0.0
+    w32 = w.astype(np.float32)
+    d = dev()
+    p, fidx, flags = W.quantize_weight(torch.from_numpy(w32).to(d), None, None, g)
+    torch.cuda.synchronize()
+    assert int(flags[0]) == 0
+    qd = O.unpack(p.codes.cpu().numpy()); sd = p.scales.cpu().numpy().astype(np.float64)
+    fd = fidx.cpu().numpy()
+    assert np.all(qd[3] == 0) and np.all(sd[3] == 0) and np.all(fd[3] == 0)
+    r = O.residual(w32, np.zeros((n, 0)), np.zeros((k, 0)))
+    res = O.quantize_residual(r, g)
+    rep = O.check_device_quant(r, res, g, qd, sd, fd)
+    assert rep["ok"], rep
+
+
+def test_quantize_flags():
+    import w4_gemm_amd as W
+    d = dev()
+    w = torch.zeros((16, 256), dtype=torch.float32, device=d)
+    w[2, 7] = float("nan")
+    _, _, flags = W.quantize_weight(w, None, None, 32)
+    torch.cuda.synchronize()
+    assert int(flags[0]) & 1
+    w = torch.zeros((16, 256), dtype=torch.float32, device=d)
+    w[5, :] = 1e6                      # rotated values 1e6*16 -> absmax/7 > 65504
+    _, _, flags = W.quantize_weight(w, None, None, 32)
+    torch.cuda.synchronize()
+    assert int(flags[0]) & 2
+
+
+def test_reconstruct_tiny(tiny):
+    import w4_gemm_amd as W
+    t = tiny
+    p = to_dev_payload(t["codes"], t["scales"], t["upb"], t["dnb"], 32)
+    what = W.reconstruct_bf16(p)
+    torch.cuda.synchronize()
+    got = bf16_tensor_to_f64(what)
+    q, s, up, dn = payload_fp64(t["codes"], t["scales"], t["upb"], t["dnb"])
+    exact = O.reconstruct(q, s, up, dn, 32)
+    ref = O.bf16_round(exact)
+    assert O.rel_fro(got, ref) <= WHAT_TOL
+    assert np.all(np.abs(got - ref) <= ulp_bf16(ref))
+    assert O.cosine(got, exact) > 0.99999
+
+
+def _fwd_checks(xbits, codes, scales, upb, dnb, group, rows=None, tag=""):
+    import w4_gemm_amd as W
+    p = to_dev_payload(codes, scales, upb, dnb, group)
+    xd = _x_dev(xbits)
+    y32 = W.linear_fwd(xd, p, torch.float32)
+    y16 = W.linear_fwd(xd, p, torch.bfloat16)
+    torch.cuda.synchronize()
+    y32h = y32.cpu().numpy().astype(np.float64)
+    y16h = bf16_tensor_to_f64(y16)
+    assert np.all(np.isfinite(y32h))
+    # bf16 output is RNE of the fp32 output, bit for bit
+    assert np.array_equal(y16h, O.bf16_round(y32h))
+    rows = np.arange(xbits.shape[0]) if rows is None else rows
+    x = O.bf16_decode(xbits[rows])
+    q, s, up, dn = payload_fp64(codes, scales, upb, dnb)
+    ref = O.forward(x, q, s, up, dn, group)
+    diag = O.forward_fp16_operands(x, q, s, up, dn, group)
+    got = y32h[rows]
+    e, cs, ed = O.rel_fro(got, ref), O.cosine(got, ref), O.rel_fro(got, diag)
+    print(f"{tag}: relF={e:.3e} cos={cs:.7f} vs-fp16-operands={ed:.3e}")
+    assert e <= Y_TOL and cs >= COS_TOL and ed <= DIAG_TOL
+    return y32h
+
+
+def test_fwd_tiny(tiny):
+    t = tiny
+    _fwd_checks(t["xbits"], t["codes"], t["scales"], t["upb"], t["dnb"], 32, tag="cfg1")
+
+
+def test_fwd_ragged_and_rank0():
+    rng = np.random.default_rng(5)
+    for (m, n, k, g, rank) in [(100, 200, 768, 64, 32), (3, 16, 256, 32, 0), (130, 33, 512, 32, 64)]:
+        codes, scales, upb, dnb = gen_payload(rng, n, k, g, max(rank, 1))
+        if rank == 0:
+            upb = dnb = None
+        from synth import gen_activations
+        xbits = gen_activations(rng, m, k, 0.01)
+        _fwd_checks(xbits, codes, scales, upb, dnb, g, tag=f"m{m} n{n} k{k} g{g} r{rank}")
+
+
+def test_fwd_zero_rows_and_large_activations():
+    import w4_gemm_amd as W
+    rng = np.random.default_rng(6)
+    codes, scales, upb, dnb = gen_payload(rng, 64, 512, 32, 32)
+    from synth import f32_to_bf16_bits
+    x = rng.standard_normal((20, 512)).astype(np.float32)
+    x[4] = 0.0                                       # an all-zero row
+    x[7] *= 3.0e4                                    # far outside fp16 range after rotation
+    x[9] *= 1e-30                                    # tiny row
+    _fwd_checks(f32_to_bf16_bits(x), codes, scales, upb, dnb, 32, tag="edge rows")
+    # m == 0 is a no-op
+    p = to_dev_payload(codes, scales, upb, dnb, 32)
+    y = torch.empty((0, 64), device=dev())
+    W.linear_fwd(torch.empty((0, 512), dtype=torch.bfloat16, device=dev()), p, out=y)
+
+
+def test_determinism(tiny):
+    import w4_gemm_amd as W
+    t = tiny
+    p = to_dev_payload(t["codes"], t["scales"], t["upb"], t["dnb"], 32)
+    xd = _x_dev(t["xbits"])
+    a = W.linear_fwd(xd, p); b = W.linear_fwd(xd, p)
+    ra = W.reconstruct_bf16(p); rb = W.reconstruct_bf16(p)
+    wt = torch.from_numpy(t["w"]).to(dev())
+    q1, f1, _ = W.quantize_weight(wt, p.up, p.down, 32)
+    q2, f2, _ = W.quantize_weight(wt, p.up, p.down, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ra.view(torch.int16), rb.view(torch.int16))
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(f1, f2)
+    assert torch.equal(q1.scales.view(torch.int16), q2.scales.view(torch.int16))
+
+
+# ------------------------------------------------------------------ full-size shapes
+@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
+def test_fwd_full_size_sampled(cfg_id):
+    cfg = CONFIGS[cfg_id]
+    rng = np.random.default_rng(100 + cfg_id)
+    codes, scales, upb, dnb = gen_payload(rng, cfg.N, cfg.K, cfg.group, cfg.rank)
+    from synth import gen_activations
+    xbits = gen_activations(np.random.default_rng(cfg_id), cfg.M, cfg.K, cfg.outlier_frac)
+    rows = np.sort(np.random.default_rng(7).choice(cfg.M, 24, replace=False))
+    _fwd_checks(xbits, codes, scales, upb, dnb, cfg.group, rows=rows, tag=f"cfg{cfg_id}")
+    if cfg.small_m:
+        for m in cfg.small_m:
+            _fwd_checks(xbits[:m], codes, scales, upb, dnb, cfg.group,
+                        rows=np.arange(min(m, 16)), tag=f"cfg{cfg_id} M={m}")
+
+
+@pytest.mark.parametrize("cfg_id", [2, 4, 5])
+def test_reconstruct_full_size_sampled(cfg_id):
+    import w4_gemm_amd as W
+    cfg = CONFIGS[cfg_id]
+    rng = np.random.default_rng(200 + cfg_id)
+    codes, scales, upb, dnb = gen_payload(rng, cfg.N, cfg.K, cfg.group, cfg.rank)
+    p = to_dev_payload(codes, scales, upb, dnb, cfg.group)
+    what = W.reconstruct_bf16(p)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(8).choice(cfg.N, 48, replace=False))
+    got = bf16_tensor_to_f64(what[torch.from_numpy(rows).to(dev())])
+    q, s, up, dn = payload_fp64(codes[rows], scales[rows], upb[rows], dnb)
+    exact = O.reconstruct(q, s, up, dn, cfg.group)
+    ref = O.bf16_round(exact)
+    e = O.rel_fro(got, ref)
+    print(f"cfg{cfg_id} reconstruct relF vs bf16(oracle) = {e:.3e}")
+    assert e <= WHAT_TOL
+    assert np.all(np.abs(got - ref) <= ulp_bf16(ref))
+
+
+def test_quantize_cfg3_sampled_rows():
+    # the fused-QKV weight (9216 x 3072, g64): whole weight on the GPU, oracle on sampled rows
+    cfg, w, _ = gen_layer(3, seed=0, with_x=False)
+    up, dn = O.svd_init(w, cfg.rank)
+    rows = np.sort(np.random.default_rng(9).choice(cfg.N, 192, replace=False))
+    import w4_gemm_amd as W
+    d = dev()
+    p, fidx, flags = W.quantize_weight(torch.from_numpy(w).to(d),
+                                       torch.from_numpy(bf16_bits_of(up).view(np.int16)).view(torch.bfloat16).to(d),
+                                       torch.from_numpy(bf16_bits_of(dn).view(np.int16)).view(torch.bfloat16).to(d),
+                                       cfg.group)
+    torch.cuda.synchronize()
+    assert int(flags[0]) == 0
+    r = O.residual(w[rows], up[rows], dn)
+    res = O.quantize_residual(r, cfg.group)
+    rep = O.check_device_quant(r, res, cfg.group, O.unpack(p.codes[torch.from_numpy(rows).to(d)].cpu().numpy()),
+                               p.scales[torch.from_numpy(rows).to(d)].cpu().numpy().astype(np.float64),
+                               fidx[torch.from_numpy(rows).to(d)].cpu().numpy())
+    print("cfg3 quantize", rep)
+    assert rep["ok"], rep

@@ -336,7 +336,7 @@ def pin_group_granularity():
 
 def pin_certification():
     rng = np.random.default_rng(13)
-    r = rng.standard_normal((32, 512)) * 0.01
+    r = rng.standard_normal((64, 512)) * 0.01
     res = O.quantize_residual(r, 32)
     rep = O.check_device_quant(r, res, 32, res.q, res.scale, res.fidx)
     assert rep["ok"] and rep["differ"] == 0
@@ -355,6 +355,20 @@ def pin_certification():
     seg = slice(gi[1] * 32, gi[1] * 32 + 32)
     qd[gi[0], seg] = O.codes_for_scale(r[gi[0], seg], sd[gi[0], gi[1]])
     assert not O.check_device_quant(r, res, 32, qd, sd, fd)["ok"]
+    # the chosen scale rounded the other way: admissible only at a scale near-tie
+    S = O.sq_oracle
+    v = O.candidate_scale_exact(res.absmax, res.fidx)
+    marg = S._fp16_boundary_margin(v)
+    lo, hi = S._fp16_bracket(v)
+    other = np.where(res.scale == lo, hi, lo)
+    for want_ok, pick in ((True, np.argwhere(marg <= S.SCALE_MARGIN)[0]),
+                          (False, np.argwhere(cert & (marg > 1e-4))[0])):
+        i, g = pick
+        sd = res.scale.copy(); sd[i, g] = other[i, g]
+        qd = res.q.copy()
+        seg = slice(g * 32, g * 32 + 32)
+        qd[i, seg] = O.codes_for_scale(r[i, seg], sd[i, g])
+        assert O.check_device_quant(r, res, 32, qd, sd, res.fidx)["ok"] == want_ok
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

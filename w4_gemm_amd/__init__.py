@@ -1,0 +1,15 @@
+"""MI355X-native SquareQ v3 W4 linear layer: libsq (HIP, gfx950) + a thin binding.
+
+Entry points (C ABI in include/sq.h, same names here):
+  sq_quantize_weight   builder side: rotate + MSE fraction sweep + int4 pack
+  sq_linear_fwd        fused forward  y = H256(x) dequant(R)^T + (x down) up^T
+  sq_reconstruct_bf16  backward side: bf16 W_hat from the same payload
+The rank-32 SVD split that feeds the quantizer is a host step (svd_init).
+"""
+from .api import (W4Payload, empty_payload, fwd_workspace_bytes, linear_fwd, quantize_weight,
+                  reconstruct_bf16)
+from ._lib import SqError, abi_version
+from .svd_init import svd_init
+
+__all__ = ["W4Payload", "empty_payload", "fwd_workspace_bytes", "linear_fwd", "quantize_weight",
+           "reconstruct_bf16", "SqError", "abi_version", "svd_init"]

@@ -1,0 +1,113 @@
+"""ctypes binding of libsq (include/sq.h).  Argument marshalling only.
+
+The library must have been built (``python -m w4_gemm_amd.build``); there is
+no fallback of any kind when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsq.so")
+
+SQ_OK = 0
+SQ_F32, SQ_BF16 = 0, 1
+SQ_FLAG_NONFINITE, SQ_FLAG_SCALE_OVERFLOW = 1, 2
+STATUS_NAMES = {0: "SQ_OK", 1: "SQ_E_NULL", 2: "SQ_E_SHAPE", 3: "SQ_E_GROUP", 4: "SQ_E_RANK",
+                5: "SQ_E_ALIGN", 6: "SQ_E_WORKSPACE", 7: "SQ_E_DTYPE", 8: "SQ_E_ARCH",
+                9: "SQ_E_HIP"}
+
+# every symbol include/sq.h declares
+EXPORTS = ("sq_quantize_weight", "sq_linear_fwd_workspace_bytes", "sq_linear_fwd",
+           "sq_linear_fwd_rotate", "sq_linear_fwd_contract", "sq_reconstruct_bf16",
+           "sq_status_str", "sq_abi_version")
+
+
+class SqW4(ctypes.Structure):
+    """Mirror of sq_w4_t."""
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("group", ctypes.c_int32),
+        ("rank", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("lora_up", ctypes.c_void_p),
+        ("lora_down", ctypes.c_void_p),
+    ]
+
+
+class SqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_str(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m w4_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.sq_quantize_weight.argtypes = [vp, ctypes.POINTER(SqW4), vp, vp, vp]
+        L.sq_quantize_weight.restype = ctypes.c_int
+        L.sq_linear_fwd_workspace_bytes.argtypes = [i64, ctypes.POINTER(SqW4)]
+        L.sq_linear_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.sq_linear_fwd.argtypes = [vp, i64, ctypes.POINTER(SqW4), vp, ctypes.c_int, vp,
+                                    ctypes.c_size_t, vp]
+        L.sq_linear_fwd.restype = ctypes.c_int
+        L.sq_linear_fwd_rotate.argtypes = [vp, i64, ctypes.POINTER(SqW4), vp, ctypes.c_size_t, vp]
+        L.sq_linear_fwd_rotate.restype = ctypes.c_int
+        L.sq_linear_fwd_contract.argtypes = [i64, ctypes.POINTER(SqW4), vp, ctypes.c_int, vp,
+                                             ctypes.c_size_t, vp]
+        L.sq_linear_fwd_contract.restype = ctypes.c_int
+        L.sq_reconstruct_bf16.argtypes = [ctypes.POINTER(SqW4), vp, vp]
+        L.sq_reconstruct_bf16.restype = ctypes.c_int
+        L.sq_status_str.argtypes = [ctypes.c_int]
+        L.sq_status_str.restype = ctypes.c_char_p
+        L.sq_abi_version.argtypes = []
+        L.sq_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().sq_status_str(status).decode()
+
+
+def abi_version() -> int:
+    return lib().sq_abi_version()
+
+
+def sq_quantize_weight(w, p: SqW4, fidx, dev_flags, stream) -> int:
+    return lib().sq_quantize_weight(w, ctypes.byref(p), fidx, dev_flags, stream)
+
+
+def sq_linear_fwd_workspace_bytes(m: int, p: SqW4) -> int:
+    return lib().sq_linear_fwd_workspace_bytes(m, ctypes.byref(p))
+
+
+def sq_linear_fwd(x, m: int, p: SqW4, y, y_dtype: int, workspace, workspace_bytes: int,
+                  stream) -> int:
+    return lib().sq_linear_fwd(x, m, ctypes.byref(p), y, y_dtype, workspace, workspace_bytes,
+                               stream)
+
+
+def sq_linear_fwd_rotate(x, m: int, p: SqW4, workspace, workspace_bytes: int, stream) -> int:
+    return lib().sq_linear_fwd_rotate(x, m, ctypes.byref(p), workspace, workspace_bytes, stream)
+
+
+def sq_linear_fwd_contract(m: int, p: SqW4, y, y_dtype: int, workspace, workspace_bytes: int,
+                           stream) -> int:
+    return lib().sq_linear_fwd_contract(m, ctypes.byref(p), y, y_dtype, workspace,
+                                        workspace_bytes, stream)
+
+
+def sq_reconstruct_bf16(p: SqW4, w_hat, stream) -> int:
+    return lib().sq_reconstruct_bf16(ctypes.byref(p), w_hat, stream)

@@ -1,0 +1,139 @@
+"""Thin torch-facing wrappers over the C ABI (include/sq.h).
+
+PyTorch only allocates device memory and supplies the current HIP stream;
+every step of the layer runs in libsq's kernels.  Each call raises SqError on a
+non-OK status.  Tensors must live on the current device.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import SqError, SqW4, SQ_BF16, SQ_F32
+
+
+@dataclass
+class W4Payload:
+    """Device tensors of one W4 layer (layouts as in sq.h)."""
+    codes: torch.Tensor      # uint8 [N, K/2]
+    scales: torch.Tensor     # float16 [N, K/group]
+    up: torch.Tensor | None  # bfloat16 [N, rank]
+    down: torch.Tensor | None  # bfloat16 [K, rank]
+    group: int
+
+    @property
+    def n(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.codes.shape[1] * 2
+
+    @property
+    def rank(self) -> int:
+        return 0 if self.up is None else self.up.shape[1]
+
+    def abi(self) -> SqW4:
+        _require(self.codes, torch.uint8, "codes")
+        _require(self.scales, torch.float16, "scales")
+        if self.up is not None:
+            _require(self.up, torch.bfloat16, "up")
+            _require(self.down, torch.bfloat16, "down")
+        return SqW4(self.n, self.k, self.group, self.rank, _ptr(self.codes), _ptr(self.scales),
+                    _ptr(self.up), _ptr(self.down))
+
+
+def _require(t, dtype, name):
+    """The C ABI takes dense row-major device buffers: refuse anything else."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != _lib.SQ_OK:
+        raise SqError(status, where)
+
+
+def empty_payload(n: int, k: int, group: int, rank: int, device="cuda") -> W4Payload:
+    up = torch.empty((n, rank), dtype=torch.bfloat16, device=device) if rank else None
+    down = torch.empty((k, rank), dtype=torch.bfloat16, device=device) if rank else None
+    return W4Payload(torch.empty((n, k // 2), dtype=torch.uint8, device=device),
+                     torch.empty((n, k // group), dtype=torch.float16, device=device),
+                     up, down, group)
+
+
+def quantize_weight(w: torch.Tensor, up: torch.Tensor | None, down: torch.Tensor | None,
+                    group: int, want_fidx: bool = True):
+    """sq_quantize_weight: fp32 W [N,K] and bf16 factors -> (payload, fidx, flags tensor)."""
+    _require(w, torch.float32, "w")
+    n, k = w.shape
+    rank = 0 if up is None else up.shape[1]
+    p = empty_payload(n, k, group, rank, w.device)
+    p.up, p.down = up, down
+    fidx = torch.empty((n, k // group), dtype=torch.uint8, device=w.device) if want_fidx else None
+    flags = torch.zeros(4, dtype=torch.int32, device=w.device)
+    _check(_lib.sq_quantize_weight(w.data_ptr(), p.abi(), _ptr(fidx), flags.data_ptr(), _stream()),
+           "sq_quantize_weight")
+    return p, fidx, flags
+
+
+def fwd_workspace_bytes(m: int, p: W4Payload) -> int:
+    return _lib.sq_linear_fwd_workspace_bytes(m, p.abi())
+
+
+def linear_fwd(x: torch.Tensor, p: W4Payload, out_dtype=torch.float32,
+               workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """sq_linear_fwd: bf16 x [M,K] -> y [M,N] (fp32 or bf16)."""
+    _require(x, torch.bfloat16, "x")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, p.n), dtype=out_dtype, device=x.device)
+    _require(out, out.dtype, "out")
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (m, p.n):
+        raise ValueError("out must be fp32 or bf16 of shape [M, N]")
+    dt = SQ_BF16 if out.dtype == torch.bfloat16 else SQ_F32
+    nbytes = fwd_workspace_bytes(m, p)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check(_lib.sq_linear_fwd(x.data_ptr(), m, p.abi(), out.data_ptr(), dt, workspace.data_ptr(),
+                              workspace.numel(), _stream()), "sq_linear_fwd")
+    return out
+
+
+def linear_fwd_rotate(x: torch.Tensor, p: W4Payload, workspace: torch.Tensor):
+    """sq_linear_fwd_rotate: the activation half of the forward, into `workspace`."""
+    _require(x, torch.bfloat16, "x")
+    _check(_lib.sq_linear_fwd_rotate(x.data_ptr(), x.shape[0], p.abi(), workspace.data_ptr(),
+                                     workspace.numel(), _stream()), "sq_linear_fwd_rotate")
+
+
+def linear_fwd_contract(m: int, p: W4Payload, out: torch.Tensor, workspace: torch.Tensor):
+    """sq_linear_fwd_contract: the weight half of the forward, from `workspace` into out."""
+    _require(out, out.dtype, "out")
+    dt = SQ_BF16 if out.dtype == torch.bfloat16 else SQ_F32
+    _check(_lib.sq_linear_fwd_contract(m, p.abi(), out.data_ptr(), dt, workspace.data_ptr(),
+                                       workspace.numel(), _stream()), "sq_linear_fwd_contract")
+    return out
+
+
+def reconstruct_bf16(p: W4Payload, out: torch.Tensor | None = None):
+    """sq_reconstruct_bf16: payload -> bf16 W_hat [N,K]."""
+    if out is None:
+        out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device=p.codes.device)
+    _require(out, torch.bfloat16, "out")
+    _check(_lib.sq_reconstruct_bf16(p.abi(), out.data_ptr(), _stream()), "sq_reconstruct_bf16")
+    return out

@@ -1,0 +1,154 @@
+// C ABI of libsq: argument validation, device check and kernel launches.
+// Every entry point validates synchronously and launches nothing on error;
+// work is enqueued on the caller's stream and never synchronized here.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/sq.h"
+#include "sq_kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+std::mutex g_arch_mu;
+
+sq_status_t check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SQ_E_HIP;
+  std::lock_guard<std::mutex> lock(g_arch_mu);
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SQ_E_HIP;
+    g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return g_arch_ok[dev] == 1 ? SQ_OK : SQ_E_ARCH;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+sq_status_t check_payload(const sq_w4_t* p, bool need_codes) {
+  if (!p) return SQ_E_NULL;
+  if (p->k < 256 || p->k % 256 != 0 || p->n < 1) return SQ_E_SHAPE;
+  if (p->group != 32 && p->group != 64) return SQ_E_GROUP;
+  if (p->rank != 0 && p->rank != 32 && p->rank != 64) return SQ_E_RANK;
+  if (!p->codes || !p->scales) return SQ_E_NULL;
+  if (p->rank > 0 && (!p->lora_up || !p->lora_down)) return SQ_E_NULL;
+  if (!aligned16(p->codes) || !aligned16(p->scales)) return SQ_E_ALIGN;
+  if (p->rank > 0 && (!aligned16(p->lora_up) || !aligned16(p->lora_down))) return SQ_E_ALIGN;
+  (void)need_codes;
+  return SQ_OK;
+}
+
+sq_status_t from_hip(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int sq_abi_version(void) { return SQ_ABI_VERSION; }
+
+const char* sq_status_str(sq_status_t s) {
+  switch (s) {
+    case SQ_OK: return "ok";
+    case SQ_E_NULL: return "a required pointer is NULL";
+    case SQ_E_SHAPE: return "bad shape: need K % 256 == 0, K >= 256, N >= 1, M >= 0";
+    case SQ_E_GROUP: return "group must be 32 or 64";
+    case SQ_E_RANK: return "rank must be 0, 32 or 64";
+    case SQ_E_ALIGN: return "every pointer must be 16-byte aligned";
+    case SQ_E_WORKSPACE: return "workspace smaller than sq_linear_fwd_workspace_bytes()";
+    case SQ_E_DTYPE: return "output dtype must be SQ_F32 or SQ_BF16";
+    case SQ_E_ARCH: return "the current device is not gfx950 (MI355X)";
+    case SQ_E_HIP: return "a HIP runtime call or kernel launch failed";
+  }
+  return "unknown status";
+}
+
+sq_status_t sq_quantize_weight(const float* w, const sq_w4_t* p, uint8_t* fidx,
+                               int32_t* dev_flags, void* stream) {
+  sq_status_t st = check_payload(p, true);
+  if (st != SQ_OK) return st;
+  if (!w || !dev_flags) return SQ_E_NULL;
+  if (!aligned16(w) || (fidx && !aligned16(fidx)) || !aligned16(dev_flags)) return SQ_E_ALIGN;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_quantize(w, p->lora_up, p->lora_down, p->codes, p->scales, fidx,
+                                      dev_flags, p->n, p->k, p->group, p->rank,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t sq_linear_fwd_workspace_bytes(int64_t m, const sq_w4_t* p) {
+  if (!p || m <= 0 || p->k < 256 || p->k % 256 || p->n < 1) return 0;
+  return sq::plan_fwd(m, p->n, p->k, p->group, p->rank).total;
+}
+
+static sq_status_t check_fwd(int64_t m, const sq_w4_t* p, void* workspace, size_t ws_bytes,
+                             sq::FwdPlan* plan) {
+  sq_status_t st = check_payload(p, true);
+  if (st != SQ_OK) return st;
+  if (m < 0) return SQ_E_SHAPE;
+  if (m == 0) return SQ_OK;
+  if (!workspace) return SQ_E_NULL;
+  if (!aligned16(workspace)) return SQ_E_ALIGN;
+  *plan = sq::plan_fwd(m, p->n, p->k, p->group, p->rank);
+  if (ws_bytes < plan->total) return SQ_E_WORKSPACE;
+  return SQ_OK;
+}
+
+sq_status_t sq_linear_fwd_rotate(const uint16_t* x, int64_t m, const sq_w4_t* p, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  sq::FwdPlan plan{};
+  sq_status_t st = check_fwd(m, p, workspace, workspace_bytes, &plan);
+  if (st != SQ_OK || m == 0) return st;
+  if (!x) return SQ_E_NULL;
+  if (!aligned16(x)) return SQ_E_ALIGN;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_fwd_rotate(plan, x, p->lora_down, workspace,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+sq_status_t sq_linear_fwd_contract(int64_t m, const sq_w4_t* p, void* y, sq_dtype_t y_dtype,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  sq::FwdPlan plan{};
+  if (y_dtype != SQ_F32 && y_dtype != SQ_BF16) return SQ_E_DTYPE;
+  sq_status_t st = check_fwd(m, p, workspace, workspace_bytes, &plan);
+  if (st != SQ_OK || m == 0) return st;
+  if (!y) return SQ_E_NULL;
+  if (!aligned16(y)) return SQ_E_ALIGN;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_fwd_contract(plan, p->codes, p->scales, p->lora_up, y,
+                                          y_dtype == SQ_BF16, workspace,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+sq_status_t sq_linear_fwd(const uint16_t* x, int64_t m, const sq_w4_t* p, void* y,
+                          sq_dtype_t y_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (y_dtype != SQ_F32 && y_dtype != SQ_BF16) return SQ_E_DTYPE;
+  sq::FwdPlan plan{};
+  sq_status_t st = check_fwd(m, p, workspace, workspace_bytes, &plan);
+  if (st != SQ_OK || m == 0) return st;
+  if (!x || !y) return SQ_E_NULL;
+  if (!aligned16(x) || !aligned16(y)) return SQ_E_ALIGN;
+  if ((st = check_device()) != SQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = from_hip(sq::launch_fwd_rotate(plan, x, p->lora_down, workspace, s))) != SQ_OK)
+    return st;
+  return from_hip(sq::launch_fwd_contract(plan, p->codes, p->scales, p->lora_up, y,
+                                          y_dtype == SQ_BF16, workspace, s));
+}
+
+sq_status_t sq_reconstruct_bf16(const sq_w4_t* p, uint16_t* w_hat, void* stream) {
+  sq_status_t st = check_payload(p, true);
+  if (st != SQ_OK) return st;
+  if (!w_hat) return SQ_E_NULL;
+  if (!aligned16(w_hat)) return SQ_E_ALIGN;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_reconstruct(p->codes, p->scales, p->lora_up, p->lora_down, w_hat,
+                                         p->n, p->k, p->group, p->rank,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Device helpers shared by the libsq kernels (gfx950, wave64).
+//
+// Lane layout used by the reconstruct, quantize and activation-rotation
+// kernels: one wave covers 16 rows x one 256-wide Hadamard block.  Lane l owns
+// row (l % 16) and the 64 consecutive columns 64*(l/16) .. 64*(l/16)+63 of the
+// block, held in 64 registers.  The Hadamard butterflies over the low six
+// column bits are therefore in-register; the two high bits live in lane bits 4
+// and 5 and are exchanged across lanes.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float fp16_bits_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// ---------------------------------------------------------------------------
+// Hadamard-256 butterflies in the 16-rows x 256-columns wave layout.
+// Unnormalized: after both halves every lane holds S @ v for its block slice,
+// S the Sylvester matrix (entries +-1); the caller applies the 1/16.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fwht_inreg64(float (&v)[64]) {
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// Column bits 6 and 7 (lane bits 4 and 5).  For a pair (a in the lane with the
+// bit clear, b in its partner) the lane with the bit clear needs a+b and the
+// other a-b; both are partner + sign*mine with sign = +1 / -1.
+__device__ __forceinline__ void fwht_cross64(float (&v)[64], int lane) {
+  const float s16 = (lane & 16) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    // bitmask swizzle: and 0x1f, xor 0x10 -> partner lane ^ 16 (within 32)
+    float p = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v[i]), 0x401F));
+    v[i] = __builtin_fmaf(s16, v[i], p);
+  }
+  const float s32 = (lane & 32) ? -1.0f : 1.0f;
+  const int addr = (lane ^ 32) << 2;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    float p = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v[i])));
+    v[i] = __builtin_fmaf(s32, v[i], p);
+  }
+}
+
+__device__ __forceinline__ void fwht256_wave(float (&v)[64], int lane) {
+  fwht_inreg64(v);
+  fwht_cross64(v, lane);
+}
+
+// Low-rank product for the wave's 16 rows x 256 columns, accumulated into the
+// wave layout above:
+//   v[4t+i] += sign * sum_r up[row0 + l%16][r] * down[col0 + 64*(l/16) + 4t + i][r]
+// on bf16 MFMA (exact products, fp32 sums), with v as the accumulator input.
+// The MFMA's row index rho = 4*(l/16)+i of tile t is mapped to column
+// 64*(rho/4) + 4t + rho%4, so each lane's 64 consecutive columns line up with
+// its registers.  sign = -1 flips the bf16 sign bits of `down` (exact).
+// Rows of `up` at or beyond n_rows read as zero; rank is a multiple of 32.
+__device__ __forceinline__ void lowrank_acc_16x256(float (&v)[64], const uint16_t* __restrict__ up,
+                                                   const uint16_t* __restrict__ down, int64_t row0,
+                                                   int64_t n_rows, int64_t col0, int rank,
+                                                   bool negate, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+  const uint32_t flip = negate ? 0x80008000u : 0u;
+  for (int rr = 0; rr < rank; rr += 32) {
+    // B operand (k = r, col = output row): lane holds up[row0 + c][rr + 8g .. +8]
+    bf16x8 bfrag;
+    if (row0 + c < n_rows) {
+      bfrag = *reinterpret_cast<const bf16x8*>(up + (row0 + c) * rank + rr + 8 * g);
+    } else {
+      bfrag = (bf16x8){};
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      // A operand (row rho = c, k = r): down row of column 64*(c/4) + 4t + c%4
+      const int64_t col = col0 + 64 * (c >> 2) + 4 * t + (c & 3);
+      u32x4 raw = *reinterpret_cast<const u32x4*>(down + col * rank + rr + 8 * g);
+      raw ^= (u32x4){flip, flip, flip, flip};
+      const bf16x8 afrag = __builtin_bit_cast(bf16x8, raw);
+      f32x4 acc = {v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag, acc, 0, 0, 0);
+      v[4 * t] = acc[0];
+      v[4 * t + 1] = acc[1];
+      v[4 * t + 2] = acc[2];
+      v[4 * t + 3] = acc[3];
+    }
+  }
+}
+
+}  // namespace sq

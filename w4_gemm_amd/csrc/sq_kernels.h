@@ -1,0 +1,32 @@
+// Host-side launchers of the libsq kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sq {
+
+hipError_t launch_reconstruct(const uint8_t* codes, const uint16_t* scales, const uint16_t* up,
+                              const uint16_t* down, uint16_t* w_hat, int64_t n, int64_t k,
+                              int group, int rank, hipStream_t stream);
+
+hipError_t launch_quantize(const float* w, const uint16_t* up, const uint16_t* down,
+                           uint8_t* codes, uint16_t* scales, uint8_t* fidx, int32_t* flags,
+                           int64_t n, int64_t k, int group, int rank, hipStream_t stream);
+
+// Forward: workspace layout and launch.
+struct FwdPlan {
+  int64_t m, n, k;
+  int group, rank;
+  int splits;          // split-K factor of the main contraction
+  int tile_m, tile_n;  // output tile of the main contraction
+  size_t off_xh, off_thi, off_tlo, off_rowscale, off_downT, off_partial, total;
+};
+FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank);
+
+hipError_t launch_fwd_rotate(const FwdPlan& plan, const uint16_t* x, const uint16_t* down,
+                             void* workspace, hipStream_t stream);
+hipError_t launch_fwd_contract(const FwdPlan& plan, const uint8_t* codes, const uint16_t* scales,
+                               const uint16_t* up, void* y, int y_bf16, void* workspace,
+                               hipStream_t stream);
+
+}  // namespace sq
