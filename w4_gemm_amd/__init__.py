@@ -6,10 +6,11 @@ Entry points (C ABI in include/sq.h, same names here):
   sq_reconstruct_bf16  backward side: bf16 W_hat from the same payload
 The rank-32 SVD split that feeds the quantizer is a host step (svd_init).
 """
-from .api import (W4Payload, empty_payload, fwd_workspace_bytes, linear_fwd, quantize_weight,
-                  reconstruct_bf16)
+from .api import (W4Payload, empty_payload, fwd_workspace_bytes, linear_fwd, linear_fwd_contract,
+                  linear_fwd_rotate, quantize_weight, reconstruct_bf16)
 from ._lib import SqError, abi_version
 from .svd_init import svd_init
 
-__all__ = ["W4Payload", "empty_payload", "fwd_workspace_bytes", "linear_fwd", "quantize_weight",
+__all__ = ["W4Payload", "empty_payload", "fwd_workspace_bytes", "linear_fwd", "linear_fwd_rotate",
+           "linear_fwd_contract", "quantize_weight",
            "reconstruct_bf16", "SqError", "abi_version", "svd_init"]

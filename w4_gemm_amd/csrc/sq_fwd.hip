@@ -27,6 +27,7 @@
 #include "sq_kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sq {
 
@@ -177,7 +178,24 @@ __global__ void __launch_bounds__(512) k_fwd_pre(const uint16_t* __restrict__ x,
 }
 
 // ---------------------------------------------------------------- main contraction
-constexpr int GBM = 128, GBN = 128, GBK = 64, LDS_STRIDE = GBK + 8;   // halves per LDS row
+// Tile configuration: BM x BN output tile per workgroup, WAVES_M x WAVES_N
+// waves, each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 16x16 MFMA
+// tiles; K advances 64 per stage (two 16x16x32 MFMA steps), double-buffered
+// in LDS.
+constexpr int GBK = 64, LDS_STRIDE = GBK + 8;   // halves per LDS row (16-byte pad)
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WM_, WAVES_N = WN_;
+  static constexpr int THREADS = 64 * WM_ * WN_;
+  static constexpr int FM = BM_ / WM_ / 16, FN = BN_ / WN_ / 16;
+  static constexpr int A_PIECES = BM_ * 8 / THREADS;   // 16-byte pieces of A per thread
+  static constexpr int B_PIECES = BN_ * 2 / THREADS;   // 32-code pieces of B per thread
+  static constexpr size_t LDS_BYTES = (size_t)2 * (BM_ + BN_) * LDS_STRIDE * 2;
+  static_assert(A_PIECES * THREADS == BM_ * 8 && B_PIECES * THREADS == BN_ * 2, "tile/threads");
+};
+
+using CfgMid = GemmCfg<128, 128, 2, 2>;
 
 // 32 packed codes (one 16-byte load) -> 16 fp16 pairs of q*s, in the permuted
 // K order: pair p of word j holds codes (8j+p, 8j+p+4).
@@ -197,64 +215,94 @@ __device__ __forceinline__ void dequant32_f16(uint32_t (&out)[16], const u32x4& 
   }
 }
 
-__global__ void __launch_bounds__(256) k_fwd_gemm(
+// Map the linear workgroup id to a tile so that the workgroups resident on one
+// XCD at a time (ids congruent mod 8 are dispatched to the same XCD) walk
+// consecutive tiles in m-major order and share their activation rows in L2.
+__device__ __forceinline__ void xcd_tile(int64_t lin, int64_t tiles, int64_t nt, int64_t& tm,
+                                         int64_t& tn) {
+  const int64_t xcd = lin & 7, idx = lin >> 3;
+  const int64_t per = tiles >> 3, rem = tiles & 7;
+  const int64_t t = xcd * per + min(xcd, rem) + idx;
+  tm = t / nt;
+  tn = t - tm * nt;
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::THREADS) k_fwd_gemm(
     const uint16_t* __restrict__ xh, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
     const uint16_t* __restrict__ tlo, const uint16_t* __restrict__ up,
     const float* __restrict__ rowscale, void* __restrict__ y, float* __restrict__ partial,
     int64_t m, int64_t n, int64_t k, int group, int rank, int splits, int y_bf16) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][GBM][LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GBN][LDS_STRIDE];
+  extern __shared__ __attribute__((aligned(16))) _Float16 lds[];
+  _Float16 (*As)[C::BM][LDS_STRIDE] = reinterpret_cast<_Float16 (*)[C::BM][LDS_STRIDE]>(lds);
+  _Float16 (*Bs)[C::BN][LDS_STRIDE] =
+      reinterpret_cast<_Float16 (*)[C::BN][LDS_STRIDE]>(lds + 2 * C::BM * LDS_STRIDE);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * GBM;
-  const int64_t n0 = (int64_t)blockIdx.x * GBN;
-  const int z = blockIdx.z;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int64_t mt = (m + C::BM - 1) / C::BM, nt = (n + C::BN - 1) / C::BN;
+  int64_t tile_m, tile_n;
+  xcd_tile(blockIdx.x, mt * nt, nt, tile_m, tile_n);
+  const int64_t m0 = tile_m * C::BM, n0 = tile_n * C::BN;
+  const int z = blockIdx.y;
   const int64_t KT = k / GBK;
   const int64_t per = (KT + splits - 1) / splits;
   const int64_t kt0 = min((int64_t)z * per, KT), kt1 = min(kt0 + per, KT);
-
-  // loader roles: row lr, half lh
-  const int lr = tid >> 1, lh = tid & 1;
-  const int64_t a_row = m0 + lr, b_row = n0 + lr;
-  const bool a_live = a_row < m, b_live = b_row < n;
   const int64_t ngroups = k / group;
+  const int64_t half_k = k >> 1;
 
-  u32x4 a_reg[4];
-  u32x4 b_reg;
-  _Float16 s_reg;
+  u32x4 a_reg[C::A_PIECES];
+  u32x4 b_reg[C::B_PIECES];
+  _Float16 s_reg[C::B_PIECES];
   auto gload = [&](int64_t kt) {
-    const int64_t kk = kt * GBK + 32 * lh;
-    if (a_live) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(xh + a_row * k + kk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) a_reg[j] = src[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) a_reg[j] = (u32x4){0, 0, 0, 0};
+    for (int p = 0; p < C::A_PIECES; ++p) {
+      const int gp = tid + C::THREADS * p;
+      const int64_t r = m0 + (gp >> 3);
+      a_reg[p] = r < m ? *reinterpret_cast<const u32x4*>(xh + r * k + kt * GBK + 8 * (gp & 7))
+                       : (u32x4){0, 0, 0, 0};
     }
-    if (b_live) {
-      b_reg = *reinterpret_cast<const u32x4*>(codes + b_row * (k >> 1) + (kk >> 1));
-      s_reg = __builtin_bit_cast(_Float16, scales[b_row * ngroups + kk / group]);
-    } else {
-      b_reg = (u32x4){0, 0, 0, 0};
-      s_reg = (_Float16)0.0f;
+#pragma unroll
+    for (int p = 0; p < C::B_PIECES; ++p) {
+      const int gp = tid + C::THREADS * p;
+      const int64_t r = n0 + (gp >> 1);
+      const int64_t kk = kt * GBK + 32 * (gp & 1);
+      if (r < n) {
+        b_reg[p] = *reinterpret_cast<const u32x4*>(codes + r * half_k + (kk >> 1));
+        s_reg[p] = __builtin_bit_cast(_Float16, scales[r * ngroups + kk / group]);
+      } else {
+        b_reg[p] = (u32x4){0, 0, 0, 0};
+        s_reg[p] = (_Float16)0.0f;
+      }
     }
   };
   auto lstore = [&](int buf) {
-    u32x4* ad = reinterpret_cast<u32x4*>(&As[buf][lr][32 * lh]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ad[j] = a_reg[j];
-    uint32_t bq[16];
-    dequant32_f16(bq, b_reg, s_reg);
-    u32x4* bd = reinterpret_cast<u32x4*>(&Bs[buf][lr][32 * lh]);
+    for (int p = 0; p < C::A_PIECES; ++p) {
+      const int gp = tid + C::THREADS * p;
+      *reinterpret_cast<u32x4*>(&As[buf][gp >> 3][8 * (gp & 7)]) = a_reg[p];
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bd[j] = (u32x4){bq[4 * j], bq[4 * j + 1], bq[4 * j + 2], bq[4 * j + 3]};
+    for (int p = 0; p < C::B_PIECES; ++p) {
+      const int gp = tid + C::THREADS * p;
+      uint32_t bq[16];
+      dequant32_f16(bq, b_reg[p], s_reg[p]);
+      u32x4* bd = reinterpret_cast<u32x4*>(&Bs[buf][gp >> 1][32 * (gp & 1)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bd[j] = (u32x4){bq[4 * j], bq[4 * j + 1], bq[4 * j + 2], bq[4 * j + 3]};
+    }
   };
 
-  f32x4 acc[4][4] = {};
+  f32x4 acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fk = 8 * (lane >> 4);
   if (kt0 < kt1) {
     gload(kt0);
     lstore(0);
@@ -265,65 +313,101 @@ __global__ void __launch_bounds__(256) k_fwd_gemm(
       if (more) gload(kt + 1);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        half8 af[4], bfr[4];
+        half8 af[C::FM];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const half8*>(&As[buf][wm * 64 + 16 * i + (lane & 15)]
-                                                     [32 * ks + 8 * (lane >> 4)]);
+        for (int i = 0; i < C::FM; ++i)
+          af[i] = *reinterpret_cast<const half8*>(
+              &As[buf][wm * (C::BM / C::WAVES_M) + 16 * i + fr][32 * ks + fk]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          bfr[j] = *reinterpret_cast<const half8*>(&Bs[buf][wn * 64 + 16 * j + (lane & 15)]
-                                                      [32 * ks + 8 * (lane >> 4)]);
+        for (int j = 0; j < C::FN; ++j) {
+          const half8 bj = *reinterpret_cast<const half8*>(
+              &Bs[buf][wn * (C::BN / C::WAVES_N) + 16 * j + fr][32 * ks + fk]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < C::FM; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bj, acc[i][j], 0, 0, 0);
+        }
       }
       if (more) lstore(buf ^ 1);
       __syncthreads();
     }
   }
 
+  const int64_t rbase = m0 + wm * (C::BM / C::WAVES_M);
+  const int64_t cbase = n0 + wn * (C::BN / C::WAVES_N);
   // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA, added once (split 0)
   if (z == 0) {
     for (int rr = 0; rr < rank; rr += 32) {
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl) {
         const uint16_t* tsrc = hl ? tlo : thi;
-        bf16x8 af[4], bfr[4];
+        bf16x8 af[C::FM], bfr[C::FN];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t r = m0 + wm * 64 + 16 * i + (lane & 15);
-          af[i] = r < m ? *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + 8 * (lane >> 4))
-                        : (bf16x8){};
+        for (int i = 0; i < C::FM; ++i) {
+          const int64_t r = rbase + 16 * i + fr;
+          af[i] = r < m ? *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + fk) : (bf16x8){};
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t cc = n0 + wn * 64 + 16 * j + (lane & 15);
-          bfr[j] = cc < n ? *reinterpret_cast<const bf16x8*>(up + cc * rank + rr + 8 * (lane >> 4))
-                          : (bf16x8){};
+        for (int j = 0; j < C::FN; ++j) {
+          const int64_t cc = cbase + 16 * j + fr;
+          bfr[j] = cc < n ? *reinterpret_cast<const bf16x8*>(up + cc * rank + rr + fk) : (bf16x8){};
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < C::FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
   }
 
   // epilogue: lane holds rows 4*(lane/16)+v of each 16x16 tile, column lane%16
+  const int lr4 = 4 * (lane >> 4);
+  if (splits == 1 && y_bf16) {
+    // stage the bf16 tile in LDS (the operand buffers are free: the loop ended
+    // with a barrier) and store whole row segments
+    constexpr int SROW = C::BN + 8;   // halves per staged row
+    uint16_t* st = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < C::FM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int lrow = wm * (C::BM / C::WAVES_M) + 16 * i + lr4 + v;
+        const int64_t r = m0 + lrow;
+        const float rs = r < m ? rowscale[r] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j)
+          st[lrow * SROW + wn * (C::BN / C::WAVES_N) + 16 * j + fr] = f32_to_bf16(acc[i][j][v] * rs);
+      }
+    }
+    __syncthreads();
+    constexpr int PIECES = C::BM * C::BN / 8;   // 16-byte pieces of the tile
+    constexpr int PER_ROW = C::BN / 8;
+#pragma unroll 4
+    for (int gp = tid; gp < PIECES; gp += C::THREADS) {
+      const int lrow = gp / PER_ROW, piece = gp % PER_ROW;
+      const int64_t r = m0 + lrow, cc = n0 + 8 * piece;
+      if (r >= m) continue;
+      const u32x4 o = *reinterpret_cast<const u32x4*>(&st[lrow * SROW + 8 * piece]);
+      uint16_t* dst = reinterpret_cast<uint16_t*>(y) + r * n + cc;
+      if (cc + 8 <= n && ((n & 7) == 0)) {
+        *reinterpret_cast<u32x4*>(dst) = o;
+      } else {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(&o);
+        for (int e = 0; e < 8 && cc + e < n; ++e) dst[e] = h[e];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int64_t r = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + v;
+      const int64_t r = rbase + 16 * i + lr4 + v;
       if (r >= m) continue;
       const float rs = rowscale[r];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t cc = n0 + wn * 64 + 16 * j + (lane & 15);
+      for (int j = 0; j < C::FN; ++j) {
+        const int64_t cc = cbase + 16 * j + fr;
         if (cc >= n) continue;
         if (splits > 1) {
           partial[((int64_t)z * m + r) * n + cc] = acc[i][j][v];
@@ -332,6 +416,293 @@ __global__ void __launch_bounds__(256) k_fwd_gemm(
         } else {
           reinterpret_cast<float*>(y)[r * n + cc] = acc[i][j][v] * rs;
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- large-tile contraction
+// 256 x 256 output tile, eight waves of 128 x 64 (8 x 4 MFMA tiles each, two
+// waves per SIMD).  Everything streams global -> LDS with direct 16-byte
+// buffer loads (no register staging), into row-major tiles of 128-byte rows
+// whose 16-byte chunk c of row r sits at slot c ^ a_swz(r):
+//  * A, the fp16 rotated activations: one stage = 64 K values = one 128-byte
+//    row per output row; double-buffered.
+//  * B, the packed codes: one super-stage = 4 stages = 256 K values = one
+//    whole 128-byte line per weight row, so every load reads full lines;
+//    double-buffered, with the matching 16 bytes of fp16 scales per row.
+// Each wave dequantizes its own B fragments (ds_read_b64 = 16 codes per lane
+// per column tile) in registers right before the MFMAs.  Within a stage, lane
+// group g = lane/16 owns K offsets 16g .. 16g+15: offsets 16g+0..7 feed the
+// first MFMA step and 16g+8..15 the second, so both operands read the same
+// 8-element chunk.  Rows/columns past the matrix edge load a clamped (valid)
+// row; their results are never stored.
+constexpr int BIG_BM = 256, BIG_BN = 256;
+#ifndef BIG_WNW
+#define BIG_WNW 4
+#endif
+constexpr int BIG_TILE_BYTES = BIG_BM * 128;     // one A stage or one B super-stage: 32 KB
+constexpr int BIG_S_BYTES = BIG_BN * 32;          // scales of one super-stage (4 KB used of 8)
+
+// The pipeline buffers are separate LDS objects so that the compiler can tell
+// a direct load into one buffer from a fragment read of another and does not
+// make the read wait for the load.
+__shared__ __attribute__((aligned(16))) uint8_t big_a0[BIG_TILE_BYTES];
+__shared__ __attribute__((aligned(16))) uint8_t big_a1[BIG_TILE_BYTES];
+__shared__ __attribute__((aligned(16))) uint8_t big_b0[BIG_TILE_BYTES];
+__shared__ __attribute__((aligned(16))) uint8_t big_b1[BIG_TILE_BYTES];
+__shared__ __attribute__((aligned(16))) uint8_t big_s0[BIG_S_BYTES];
+__shared__ __attribute__((aligned(16))) uint8_t big_s1[BIG_S_BYTES];
+
+// Slot of 16-byte chunk c in row r is c ^ a_swz(r): the 16 rows read by one
+// fragment load land in distinct bank groups whether the LDS has 32 or 64 banks.
+__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// 8 packed codes -> fp16(q*s) pairs in the permuted K order.  Per pair the
+// nibbles are selected, their sign bit flipped (q + 8) and the fp16 exponent
+// of 1024 inserted by (w & 0x000F000F) ^ 0x64086408 (one 3-input bit op);
+// then (1024 + q + 8) - 1032 is exact and * s rounds once.
+__device__ __forceinline__ half8 dequant8_f16(uint32_t word, _Float16 s) {
+  const half2v sv = {s, s};
+  const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  uint32_t o[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t w = word >> (4 * p);
+    half2v h = __builtin_bit_cast(half2v, (w & 0x000F000Fu) ^ 0x64086408u);
+    h = (h - off) * sv;
+    o[p] = __builtin_bit_cast(uint32_t, h);
+  }
+  return __builtin_bit_cast(half8, (u32x4){o[0], o[1], o[2], o[3]});
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0], expcnt [6:4], lgkmcnt [11:8])
+constexpr int WAIT_VM0 = 0x0F70, WAIT_VM5 = 0x0F75, WAIT_LGKM0 = 0xC07F;
+
+constexpr int WNW = BIG_WNW;
+template <int GSHIFT>   // log2 of the group size
+__global__ void __launch_bounds__(128 * WNW, 1) k_fwd_gemm_big(
+    const uint16_t* __restrict__ xh, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
+    const uint16_t* __restrict__ tlo, const uint16_t* __restrict__ up,
+    const float* __restrict__ rowscale, void* __restrict__ y, int64_t m, int64_t n, int64_t k,
+    int rank, int y_bf16) {
+  constexpr int gshift = GSHIFT;
+  constexpr int NWAVES = 2 * WNW;
+  constexpr int WTN = BIG_BN / WNW, FN = WTN / 16;   // wave tile: 128 x WTN
+  constexpr int ROWS_PER_WAVE = BIG_BM / NWAVES;      // rows each wave loads
+  constexpr int L_INSTR = ROWS_PER_WAVE / 8;          // 1 KB direct loads per tile per wave
+  static_assert(NWAVES == 8 && WTN == 64, "the staging epilogue assumes 8 waves of 128x64");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WNW, wn = wave % WNW;
+  const int64_t mt = (m + BIG_BM - 1) / BIG_BM, nt = (n + BIG_BN - 1) / BIG_BN;
+  int64_t tile_m, tile_n;
+  xcd_tile(blockIdx.x, mt * nt, nt, tile_m, tile_n);
+  const int64_t m0 = tile_m * BIG_BM, n0 = tile_n * BIG_BN;
+  const int64_t KT = k / GBK;
+  const int64_t half_k = k >> 1, ngroups = k >> gshift;
+  const int fr = lane & 15, g = lane >> 4;
+
+  // ---- loaders: wave w fills rows ROWS_PER_WAVE*w .. of each tile, eight
+  // rows (8 lanes x 16 bytes each) per instruction
+  const int l_row = lane >> 3, l_slot = lane & 7;
+  const int64_t a_rows = min((int64_t)BIG_BM, m - m0);
+  const int64_t b_rows = min((int64_t)BIG_BN, n - n0);
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(xh + m0 * k), (short)0, (int)(a_rows * k * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(codes + n0 * half_k), (short)0, (int)(b_rows * half_k), 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scales + n0 * ngroups), (short)0, (int)(b_rows * ngroups * 2), 0x00020000);
+  uint32_t a_off[L_INSTR], c_off[L_INSTR];
+#pragma unroll
+  for (int i = 0; i < L_INSTR; ++i) {
+    const int r = ROWS_PER_WAVE * wave + 8 * i + l_row;
+    const int64_t ra = min((int64_t)r, a_rows - 1), rb = min((int64_t)r, b_rows - 1);
+    a_off[i] = (uint32_t)(ra * k * 2) + 16 * (l_slot ^ a_swz(r));
+    c_off[i] = (uint32_t)(rb * half_k) + 16 * (l_slot ^ a_swz(r));
+  }
+  // scales: lanes l and l+32 of wave w both load the 16 bytes of row 32w + l%32
+  // (one load instruction per wave keeps the load count uniform; the upper
+  // copy is never read)
+  const int s_row = ROWS_PER_WAVE * wave + (lane & 31);
+  const uint32_t s_off = (uint32_t)(min((int64_t)s_row, b_rows - 1) * ngroups * 2);
+
+  auto a_issue = [&](int64_t kt, uint8_t* buf) {
+    uint8_t* base = buf + ROWS_PER_WAVE * wave * 128;
+#pragma unroll
+    for (int i = 0; i < L_INSTR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(base + i * 1024), 16,
+                                               a_off[i], (int)(kt * GBK * 2), 0, 0);
+  };
+  auto b_issue = [&](int64_t ss, uint8_t* bbuf, uint8_t* sbuf) {   // K 256 ss .. +256
+    uint8_t* base = bbuf + ROWS_PER_WAVE * wave * 128;
+#pragma unroll
+    for (int i = 0; i < L_INSTR; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c_rsrc, (lds_ptr_t)(base + i * 1024), 16,
+                                               c_off[i], (int)(ss * 128), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr_t)(sbuf + wave * 1024), 16, s_off,
+                                             (int)(((ss * 256) >> gshift) * 2), 0, 0);
+  };
+
+  f32x4 acc[8][FN];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  // Fragment addresses.  For rows r = a_row0 + 16 i (and b_row0 + 16 j) the
+  // swizzle a_swz(r) equals a_swz(fr), so each lane needs one base per K chunk
+  // and the row steps are immediate offsets.
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int sw = a_swz(fr);
+  const int a_row0 = 128 * wm + fr;
+  const int b_row0 = WTN * wn + fr;
+  uint32_t a_lane[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) a_lane[ks] = a_row0 * 128 + 16 * ((2 * g + ks) ^ sw);
+  // scales of row r live at (r >> 5) * 1024 + (r & 31) * 16
+  const uint32_t s_lane = (2 * wn) * 1024 + fr * 16 + 2 * ((16 * g) >> GSHIFT);
+
+  // Per stage (per wave; loads complete in issue order):
+  //   1. wait for this wave's loads of the stage (vmcnt(0)) and for its LDS
+  //      reads of the previous stage (lgkmcnt(0)); s_barrier publishes the
+  //      stage to every wave and frees the buffers the previous stage read;
+  //   2. read all fragments of the stage into registers;
+  //   3. issue the direct loads of A for the next stage (and, in stage 1 of a
+  //      super-stage, of B and scales for the next super-stage) - after the
+  //      fragment reads, so that none of them waits for these loads;
+  //   4. dequantize B and run the MFMAs.
+  // Past the end the last stage / super-stage is re-read (in bounds, never
+  // consumed), so the loop has no data-dependent branch.
+  const int64_t NSS = KT >> 2;   // K is a multiple of 256
+  a_issue(0, big_a0);
+  b_issue(0, big_b0, big_s0);
+#pragma unroll 1
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    const int s = (int)(kt & 3);
+    const int64_t ss = kt >> 2;
+    const bool aodd = kt & 1, bodd = ss & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* abase = aodd ? big_a1 : big_a0;
+    const uint8_t* bbase = bodd ? big_b1 : big_b0;
+    const uint8_t* sbase = bodd ? big_s1 : big_s0;
+    half8 af[2][8];
+    u32x2 bw[FN];
+    _Float16 bsc[FN];
+    const uint32_t b_lane = b_row0 * 128 + 16 * ((2 * s + (g >> 1)) ^ sw) + 8 * (g & 1);
+    const uint32_t s_off_st = s_lane + 2 * ((64 * s) >> GSHIFT);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      bw[j] = *reinterpret_cast<const u32x2*>(bbase + b_lane + j * 2048);
+      bsc[j] = *reinterpret_cast<const _Float16*>(sbase + s_off_st + (j >> 1) * 1024 + (j & 1) * 256);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        af[ks][i] = *reinterpret_cast<const half8*>(abase + a_lane[ks] + i * 2048);
+    __builtin_amdgcn_sched_barrier(0);
+    a_issue(min(kt + 1, KT - 1), aodd ? big_a0 : big_a1);
+    if (s == 1) b_issue(min(ss + 1, NSS - 1), bodd ? big_b0 : big_b1, bodd ? big_s0 : big_s1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const half8 bj = dequant8_f16(bw[j][ks], bsc[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ks][i], bj, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  const int64_t rbase = m0 + 128 * wm, cbase = n0 + WTN * wn;
+  // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA into the same accumulators
+  for (int rr = 0; rr < rank; rr += 32) {
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) {
+      const uint16_t* tsrc = hl ? tlo : thi;
+      bf16x8 af[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t r = min(rbase + 16 * i + fr, m - 1);
+        af[i] = *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + 8 * g);
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t c = min(cbase + 16 * j + fr, n - 1);
+        const bf16x8 bj = *reinterpret_cast<const bf16x8*>(up + c * rank + rr + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bj, acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  const int lr4 = 4 * g;
+  if (y_bf16) {
+    // Each wave stages its 128 x 64 bf16 sub-tile (16 KB, 128-byte rows with
+    // the same chunk swizzle) in one half of a pipeline buffer, then stores
+    // eight whole 128-byte row segments per instruction.
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // the final (unused) prefetches have landed
+    __syncthreads();                        // every wave is done with the pipeline buffers
+    const int wb = wave >> 1;
+    uint8_t* st = (wb == 0 ? big_a0 : wb == 1 ? big_a1 : wb == 2 ? big_b0 : big_b1) +
+                  (wave & 1) * 16384;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int lrow = 16 * i + lr4 + v;
+        const float rs = rowscale[min(rbase + lrow, m - 1)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = 16 * j + fr;   // chunk col/8, element col%8
+          *reinterpret_cast<uint16_t*>(st + lrow * 128 + 16 * ((col >> 3) ^ a_swz(lrow)) +
+                                       2 * (col & 7)) = f32_to_bf16(acc[i][j][v] * rs);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_wave_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const bool full_cols = (cbase + WTN <= n) && ((n & 7) == 0);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int lrow = 8 * it + (lane >> 3), chunk = lane & 7;
+      const int64_t r = rbase + lrow, c = cbase + 8 * chunk;
+      const u32x4 o = *reinterpret_cast<const u32x4*>(st + lrow * 128 + 16 * (chunk ^ a_swz(lrow)));
+      if (r >= m) continue;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(y) + r * n + c;
+      if (full_cols) {
+        *reinterpret_cast<u32x4*>(dst) = o;
+      } else {
+        const uint16_t* h = reinterpret_cast<const uint16_t*>(&o);
+        for (int e = 0; e < 8 && c + e < n; ++e) dst[e] = h[e];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t r = rbase + 16 * i + lr4 + v;
+      if (r >= m) continue;
+      const float rs = rowscale[r];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t c = cbase + 16 * j + fr;
+        if (c < n) reinterpret_cast<float*>(y)[r * n + c] = acc[i][j][v] * rs;
       }
     }
   }
@@ -356,18 +727,22 @@ __global__ void __launch_bounds__(256) k_fwd_reduce(const float* __restrict__ pa
 // ---------------------------------------------------------------- host side
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Tile choice: the 256x256 tile (four 128x128 waves) when it yields enough
+// workgroups to cover the chip, else 128x128 with split-K.
 FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   FwdPlan p{};
   p.m = m; p.n = n; p.k = k; p.group = group; p.rank = rank;
-  p.tile_m = GBM; p.tile_n = GBN;
-  const int64_t tiles = ((m + GBM - 1) / GBM) * ((n + GBN - 1) / GBN);
   const int64_t KT = k / GBK;
-  // enough workgroups to cover the 256 compute units about twice, but keep
-  // at least 8 K-steps per split
-  int64_t s = (512 + tiles - 1) / tiles;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, KT / 8));
-  s = std::max<int64_t>(s, 1);
-  p.splits = (int)s;
+  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
+  if (big_tiles >= 512) {
+    p.tile_m = 256; p.tile_n = 256; p.splits = 1;
+  } else {
+    p.tile_m = 128; p.tile_n = 128;
+    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
+    int64_t s = (512 + tiles - 1) / tiles;
+    s = std::min<int64_t>(s, std::max<int64_t>(1, KT / 8));
+    p.splits = (int)std::max<int64_t>(s, 1);
+  }
   size_t off = 0;
   p.off_xh = off;        off = align256(off + (size_t)m * k * 2);
   p.off_thi = off;       off = align256(off + (size_t)m * std::max(rank, 1) * 2);
@@ -414,10 +789,22 @@ hipError_t launch_fwd_contract(const FwdPlan& p, const uint8_t* codes, const uin
                                hipStream_t stream) {
   const FwdBuffers b = carve(p, workspace);
   hipError_t err;
-  dim3 grid((unsigned)((p.n + GBN - 1) / GBN), (unsigned)((p.m + GBM - 1) / GBM),
-            (unsigned)p.splits);
-  hipLaunchKernelGGL(k_fwd_gemm, grid, dim3(256), 0, stream, b.xh, codes, scales, b.thi, b.tlo, up,
-                     b.rowscale, y, b.partial, p.m, p.n, p.k, p.group, p.rank, p.splits, y_bf16);
+  const int64_t tiles = ((p.m + p.tile_m - 1) / p.tile_m) * ((p.n + p.tile_n - 1) / p.tile_n);
+  dim3 grid((unsigned)tiles, (unsigned)p.splits);
+  if (p.tile_m == 256) {
+    if (p.group == 32)
+      hipLaunchKernelGGL(k_fwd_gemm_big<5>, dim3((unsigned)tiles), dim3(128 * BIG_WNW), 0, stream,
+                         b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k,
+                         p.rank, y_bf16);
+    else
+      hipLaunchKernelGGL(k_fwd_gemm_big<6>, dim3((unsigned)tiles), dim3(128 * BIG_WNW), 0, stream,
+                         b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k,
+                         p.rank, y_bf16);
+  } else {
+    hipLaunchKernelGGL(k_fwd_gemm<CfgMid>, grid, dim3(CfgMid::THREADS), CfgMid::LDS_BYTES, stream,
+                       b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, b.partial, p.m, p.n,
+                       p.k, p.group, p.rank, p.splits, y_bf16);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (p.splits > 1) {
     const int64_t cnt = p.m * p.n;

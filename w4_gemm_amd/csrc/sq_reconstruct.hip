@@ -36,12 +36,17 @@ __device__ __forceinline__ void dequant64(float (&v)[64], const u32x4 (&w)[2], f
   }
 }
 
+// LDS staging rows: 256 bf16 = 32 x 16 bytes, padded by one 16-byte slot so
+// that the 16 rows written by one instruction start in different banks.
+constexpr int STAGE_ROW_U4 = 33;
+
 __global__ void __launch_bounds__(256) k_reconstruct(const uint8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
                                                       const uint16_t* __restrict__ up,
                                                       const uint16_t* __restrict__ down,
                                                       uint16_t* __restrict__ w_hat, int64_t n,
                                                       int64_t k, int group, int rank) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_stage[4][16][STAGE_ROW_U4 * 4];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t nblk = k >> 8;
@@ -75,19 +80,25 @@ __global__ void __launch_bounds__(256) k_reconstruct(const uint8_t* __restrict__
   fwht256_wave(v, lane);
   lowrank_acc_16x256(v, up, down, row0, n, blk * 256, rank, false, lane);
 
-  if (!live) return;
-  u32x4 out[8];
+  // Stage the wave's 16 x 256 bf16 tile in LDS so that every global store
+  // instruction writes two whole 512-byte row segments.
+  u32x4* stage = reinterpret_cast<u32x4*>(&s_stage[wave][0][0]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    u32x4 o;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 8 * j + 2 * e;
-      out[j][e] = pack_bf16x2(v[i], v[i + 1]);
-    }
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[8 * j + 2 * e], v[8 * j + 2 * e + 1]);
+    stage[c * STAGE_ROW_U4 + 8 * g + j] = o;
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(w_hat + row * k + col);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
-  for (int j = 0; j < 8; ++j) __builtin_nontemporal_store(out[j], dst + j);
+  for (int j = 0; j < 8; ++j) {
+    const int rr = 2 * j + (lane >> 5), piece = lane & 31;
+    const u32x4 o = stage[rr * STAGE_ROW_U4 + piece];
+    if (row0 + rr < n)
+      *reinterpret_cast<u32x4*>(w_hat + (row0 + rr) * k + blk * 256 + 8 * piece) = o;
+  }
 }
 
 hipError_t launch_reconstruct(const uint8_t* codes, const uint16_t* scales, const uint16_t* up,
