@@ -422,31 +422,35 @@ __global__ void __launch_bounds__(C::THREADS) k_fwd_gemm(
 }
 
 // ---------------------------------------------------------------- large-tile contraction
-// 256 x 256 output tile, eight waves of 128 x 64 (8 x 4 MFMA tiles each, two
-// waves per SIMD).  Everything streams global -> LDS with direct 16-byte
-// buffer loads (no register staging), into row-major tiles of 128-byte rows
-// whose 16-byte chunk c of row r sits at slot c ^ a_swz(r):
-//  * A, the fp16 rotated activations: one stage = 64 K values = one 128-byte
-//    row per output row; double-buffered.
-//  * B, the packed codes: one super-stage = 4 stages = 256 K values = one
-//    whole 128-byte line per weight row, so every load reads full lines;
-//    double-buffered, with the matching 16 bytes of fp16 scales per row.
-// Each wave dequantizes its own B fragments (ds_read_b64 = 16 codes per lane
-// per column tile) in registers right before the MFMAs.  Within a stage, lane
+// 256 x 256 output tile per workgroup, eight waves of 128 x 64 (8 x 4 MFMA
+// tiles each, two waves per SIMD).
+//
+// Data path: everything streams global -> LDS with direct 16-byte buffer
+// loads (no register staging) into tiles of 128-byte rows whose 16-byte chunk
+// c of row r sits at slot c ^ a_swz(r) (conflict-free fragment reads):
+//  * A, the fp16 rotated activations: one stage = 64 K values per row;
+//  * B, the packed codes: one super-stage = 4 stages = 256 K values = one full
+//    128-byte line per weight row; plus 16 bytes of fp16 scales per row.
+// Each wave dequantizes its own B fragments in registers (16 codes = one
+// 8-byte LDS read per lane per column tile and stage).  Within a stage, lane
 // group g = lane/16 owns K offsets 16g .. 16g+15: offsets 16g+0..7 feed the
 // first MFMA step and 16g+8..15 the second, so both operands read the same
-// 8-element chunk.  Rows/columns past the matrix edge load a clamped (valid)
-// row; their results are never stored.
-constexpr int BIG_BM = 256, BIG_BN = 256;
-#ifndef BIG_WNW
-#define BIG_WNW 4
-#endif
-constexpr int BIG_TILE_BYTES = BIG_BM * 128;     // one A stage or one B super-stage: 32 KB
-constexpr int BIG_S_BYTES = BIG_BN * 32;          // scales of one super-stage (4 KB used of 8)
+// 8-element chunk.
+//
+// Schedule (per wave): a stage is two half-steps of 32 MFMAs.  While the MFMAs
+// of one half-step run, the wave reads the A fragments of the next half-step
+// and dequantizes its B fragments, so LDS reads and VALU work hide under the
+// MFMAs.  The single barrier of a stage sits between its half-steps: there,
+// the loads of the next stage have landed (issued one stage earlier) and the
+// buffer of this stage has been read by every wave, so it is refilled with the
+// stage after next.  Rows and columns past the matrix edge load a clamped
+// (valid) row; their results are never stored.
+constexpr int BIG_BM = 256, BIG_BN = 256, BIG_THREADS = 512;
+constexpr int BIG_TILE_BYTES = BIG_BM * 128;   // one A stage or one B super-stage: 32 KB
+constexpr int BIG_S_BYTES = (BIG_BN + 64) * 16;  // scales of one super-stage, 16 B per row (+ tail)
 
 // The pipeline buffers are separate LDS objects so that the compiler can tell
-// a direct load into one buffer from a fragment read of another and does not
-// make the read wait for the load.
+// a direct load into one buffer from a fragment read of another.
 __shared__ __attribute__((aligned(16))) uint8_t big_a0[BIG_TILE_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t big_a1[BIG_TILE_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t big_b0[BIG_TILE_BYTES];
@@ -479,36 +483,31 @@ __device__ __forceinline__ half8 dequant8_f16(uint32_t word, _Float16 s) {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0], expcnt [6:4], lgkmcnt [11:8])
-constexpr int WAIT_VM0 = 0x0F70, WAIT_VM5 = 0x0F75, WAIT_LGKM0 = 0xC07F;
+constexpr int WAIT_VM0 = 0x0F70, WAIT_LGKM0 = 0xC07F;
 
-constexpr int WNW = BIG_WNW;
 template <int GSHIFT>   // log2 of the group size
-__global__ void __launch_bounds__(128 * WNW, 1) k_fwd_gemm_big(
+__global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     const uint16_t* __restrict__ xh, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
     const uint16_t* __restrict__ tlo, const uint16_t* __restrict__ up,
     const float* __restrict__ rowscale, void* __restrict__ y, int64_t m, int64_t n, int64_t k,
     int rank, int y_bf16) {
-  constexpr int gshift = GSHIFT;
-  constexpr int NWAVES = 2 * WNW;
-  constexpr int WTN = BIG_BN / WNW, FN = WTN / 16;   // wave tile: 128 x WTN
-  constexpr int ROWS_PER_WAVE = BIG_BM / NWAVES;      // rows each wave loads
-  constexpr int L_INSTR = ROWS_PER_WAVE / 8;          // 1 KB direct loads per tile per wave
-  static_assert(NWAVES == 8 && WTN == 64, "the staging epilogue assumes 8 waves of 128x64");
+  constexpr int FN = 4;   // wave tile 128 x 64
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WNW, wn = wave % WNW;
+  const int wm = wave >> 2, wn = wave & 3;
   const int64_t mt = (m + BIG_BM - 1) / BIG_BM, nt = (n + BIG_BN - 1) / BIG_BN;
   int64_t tile_m, tile_n;
   xcd_tile(blockIdx.x, mt * nt, nt, tile_m, tile_n);
   const int64_t m0 = tile_m * BIG_BM, n0 = tile_n * BIG_BN;
   const int64_t KT = k / GBK;
-  const int64_t half_k = k >> 1, ngroups = k >> gshift;
+  const int64_t NSS = KT >> 2;   // K is a multiple of 256
+  const int64_t half_k = k >> 1, ngroups = k >> GSHIFT;
   const int fr = lane & 15, g = lane >> 4;
 
-  // ---- loaders: wave w fills rows ROWS_PER_WAVE*w .. of each tile, eight
-  // rows (8 lanes x 16 bytes each) per instruction
-  const int l_row = lane >> 3, l_slot = lane & 7;
+  // ---- loaders: wave w fills rows 32w .. 32w+31 of each tile, eight rows
+  // (8 lanes x 16 bytes) per instruction
   const int64_t a_rows = min((int64_t)BIG_BM, m - m0);
   const int64_t b_rows = min((int64_t)BIG_BN, n - n0);
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -517,35 +516,72 @@ __global__ void __launch_bounds__(128 * WNW, 1) k_fwd_gemm_big(
       (void*)(codes + n0 * half_k), (short)0, (int)(b_rows * half_k), 0x00020000);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(scales + n0 * ngroups), (short)0, (int)(b_rows * ngroups * 2), 0x00020000);
-  uint32_t a_off[L_INSTR], c_off[L_INSTR];
+  uint32_t a_off[4];
 #pragma unroll
-  for (int i = 0; i < L_INSTR; ++i) {
-    const int r = ROWS_PER_WAVE * wave + 8 * i + l_row;
-    const int64_t ra = min((int64_t)r, a_rows - 1), rb = min((int64_t)r, b_rows - 1);
-    a_off[i] = (uint32_t)(ra * k * 2) + 16 * (l_slot ^ a_swz(r));
-    c_off[i] = (uint32_t)(rb * half_k) + 16 * (l_slot ^ a_swz(r));
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    a_off[i] = (uint32_t)(min((int64_t)r, a_rows - 1) * k * 2) + 16 * ((lane & 7) ^ a_swz(r));
   }
-  // scales: lanes l and l+32 of wave w both load the 16 bytes of row 32w + l%32
-  // (one load instruction per wave keeps the load count uniform; the upper
-  // copy is never read)
-  const int s_row = ROWS_PER_WAVE * wave + (lane & 31);
-  const uint32_t s_off = (uint32_t)(min((int64_t)s_row, b_rows - 1) * ngroups * 2);
 
   auto a_issue = [&](int64_t kt, uint8_t* buf) {
-    uint8_t* base = buf + ROWS_PER_WAVE * wave * 128;
+    uint8_t* base = buf + wave * 4096;
 #pragma unroll
-    for (int i = 0; i < L_INSTR; ++i)
+    for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(base + i * 1024), 16,
                                                a_off[i], (int)(kt * GBK * 2), 0, 0);
   };
-  auto b_issue = [&](int64_t ss, uint8_t* bbuf, uint8_t* sbuf) {   // K 256 ss .. +256
-    uint8_t* base = bbuf + ROWS_PER_WAVE * wave * 128;
+  // B arrives a quarter super-stage per stage: quarter qq (rows 64 qq .. +64 of
+  // the tile, eight per wave) of super-stage ss, plus those rows' scales
+  // (lanes 0..7 of each wave; one instruction per wave either way).
+  // (per-quarter offsets are recomputed when issued: a few VALU per stage
+  // instead of eight live registers; a_swz(r + 64 qq) = a_swz(r))
+  const int cq_slot = 16 * ((lane & 7) ^ a_swz(8 * wave + (lane >> 3)));
+  const int b_last = (int)b_rows - 1;
+  auto bq_issue = [&](int64_t ss, int qq, uint8_t* bbuf, uint8_t* sbuf) {
+    const int r = 64 * qq + 8 * wave + (lane >> 3);
+    const int sr = 64 * qq + 8 * wave + lane;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        c_rsrc, (lds_ptr_t)(bbuf + (64 * qq + 8 * wave) * 128), 16,
+        (uint32_t)min(r, b_last) * (uint32_t)half_k + cq_slot, (int)(ss * 128), 0, 0);
+    // scales: lane l writes row 64 qq + 8 wave + l (row r at r * 16); rows
+    // beyond this wave's eight get the same bytes another wave writes for
+    // them within the same refill window, and rows past 255 land in the
+    // buffer's spare tail
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        s_rsrc, (lds_ptr_t)(sbuf + (64 * qq + 8 * wave) * 16), 16,
+        (uint32_t)min(sr, b_last) * (uint32_t)(ngroups * 2), (int)(((ss * 256) >> GSHIFT) * 2), 0,
+        0);
+  };
+  auto b_issue = [&](int64_t ss, uint8_t* bbuf, uint8_t* sbuf) {
 #pragma unroll
-    for (int i = 0; i < L_INSTR; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c_rsrc, (lds_ptr_t)(base + i * 1024), 16,
-                                               c_off[i], (int)(ss * 128), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr_t)(sbuf + wave * 1024), 16, s_off,
-                                             (int)(((ss * 256) >> gshift) * 2), 0, 0);
+    for (int qq = 0; qq < 4; ++qq) bq_issue(ss, qq, bbuf, sbuf);
+  };
+
+  // Fragment addresses: for rows r = (128 wm | 64 wn) + fr + 16 i the swizzle
+  // equals a_swz(fr), so row steps are immediate offsets.
+  const int swa = a_swz(fr);
+  uint32_t a_lane[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) a_lane[ks] = (128 * wm + fr) * 128 + 16 * ((2 * g + ks) ^ swa);
+  const int b_row0 = 64 * wn + fr;
+  // scales of row r live at r * 16
+  const uint32_t s_lane = b_row0 * 16 + 2 * ((16 * g) >> GSHIFT);
+
+  auto read_a = [&](half8 (&af)[8], const uint8_t* abase, int ks) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      af[i] = *reinterpret_cast<const half8*>(abase + a_lane[ks] + i * 2048);
+  };
+  // B words (both half-steps) and scales of stage s of a super-stage
+  auto read_b = [&](u32x2 (&bw)[FN], _Float16 (&bs)[FN], const uint8_t* bbase,
+                    const uint8_t* sbase, int s) {
+    const uint32_t bl = b_row0 * 128 + 16 * ((2 * s + (g >> 1)) ^ swa) + 8 * (g & 1);
+    const uint32_t sl = s_lane + 2 * ((64 * s) >> GSHIFT);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      bw[j] = *reinterpret_cast<const u32x2*>(bbase + bl + j * 2048);
+      bs[j] = *reinterpret_cast<const _Float16*>(sbase + sl + j * 256);
+    }
   };
 
   f32x4 acc[8][FN];
@@ -553,79 +589,109 @@ __global__ void __launch_bounds__(128 * WNW, 1) k_fwd_gemm_big(
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  // Fragment addresses.  For rows r = a_row0 + 16 i (and b_row0 + 16 j) the
-  // swizzle a_swz(r) equals a_swz(fr), so each lane needs one base per K chunk
-  // and the row steps are immediate offsets.
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const int sw = a_swz(fr);
-  const int a_row0 = 128 * wm + fr;
-  const int b_row0 = WTN * wn + fr;
-  uint32_t a_lane[2];
+  auto mfma_step = [&](const half8 (&af)[8], const half8 (&bj)[FN]) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) a_lane[ks] = a_row0 * 128 + 16 * ((2 * g + ks) ^ sw);
-  // scales of row r live at (r >> 5) * 1024 + (r & 31) * 16
-  const uint32_t s_lane = (2 * wn) * 1024 + fr * 16 + 2 * ((16 * g) >> GSHIFT);
-
-  // Per stage (per wave; loads complete in issue order):
-  //   1. wait for this wave's loads of the stage (vmcnt(0)) and for its LDS
-  //      reads of the previous stage (lgkmcnt(0)); s_barrier publishes the
-  //      stage to every wave and frees the buffers the previous stage read;
-  //   2. read all fragments of the stage into registers;
-  //   3. issue the direct loads of A for the next stage (and, in stage 1 of a
-  //      super-stage, of B and scales for the next super-stage) - after the
-  //      fragment reads, so that none of them waits for these loads;
-  //   4. dequantize B and run the MFMAs.
-  // Past the end the last stage / super-stage is re-read (in bounds, never
-  // consumed), so the loop has no data-dependent branch.
-  const int64_t NSS = KT >> 2;   // K is a multiple of 256
-  a_issue(0, big_a0);
-  b_issue(0, big_b0, big_s0);
-#pragma unroll 1
-  for (int64_t kt = 0; kt < KT; ++kt) {
-    const int s = (int)(kt & 3);
-    const int64_t ss = kt >> 2;
-    const bool aodd = kt & 1, bodd = ss & 1;
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bj[j], acc[i][j], 0, 0, 0);
+  };
+  auto sync = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* abase = aodd ? big_a1 : big_a0;
-    const uint8_t* bbase = bodd ? big_b1 : big_b0;
-    const uint8_t* sbase = bodd ? big_s1 : big_s0;
-    half8 af[2][8];
+  };
+
+  // ---- prologue: stages 0 and 1 of A, super-stage 0 and the first quarter of
+  // super-stage 1 of B (the loop issues the rest)
+  a_issue(0, big_a0);
+  a_issue(min((int64_t)1, KT - 1), big_a1);
+  b_issue(0, big_b0, big_s0);
+  bq_issue(min((int64_t)1, NSS - 1), 0, big_b1, big_s1);
+  sync();
+  half8 af0[8], af1[8], bj0[FN], bj1[FN];
+  uint32_t bw1[FN];
+  _Float16 bsc[FN];
+  {
     u32x2 bw[FN];
-    _Float16 bsc[FN];
-    const uint32_t b_lane = b_row0 * 128 + 16 * ((2 * s + (g >> 1)) ^ sw) + 8 * (g & 1);
-    const uint32_t s_off_st = s_lane + 2 * ((64 * s) >> GSHIFT);
+    read_a(af0, big_a0, 0);
+    read_b(bw, bsc, big_b0, big_s0, 0);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      bw[j] = *reinterpret_cast<const u32x2*>(bbase + b_lane + j * 2048);
-      bsc[j] = *reinterpret_cast<const _Float16*>(sbase + s_off_st + (j >> 1) * 1024 + (j & 1) * 256);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        af[ks][i] = *reinterpret_cast<const half8*>(abase + a_lane[ks] + i * 2048);
-    __builtin_amdgcn_sched_barrier(0);
-    a_issue(min(kt + 1, KT - 1), aodd ? big_a0 : big_a1);
-    if (s == 1) b_issue(min(ss + 1, NSS - 1), bodd ? big_b0 : big_b1, bodd ? big_s0 : big_s1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const half8 bj = dequant8_f16(bw[j][ks], bsc[j]);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ks][i], bj, acc[i][j], 0, 0, 0);
-      }
+      bj0[j] = dequant8_f16(bw[j][0], bsc[j]);
+      bw1[j] = bw[j][1];
     }
   }
 
-  const int64_t rbase = m0 + 128 * wm, cbase = n0 + WTN * wn;
+  // Instruction interleave (sched_group_barrier masks: 0x008 MFMA, 0x100 LDS
+  // read, 0x002 VALU, 0x020 VMEM read): every MFMA is followed by a share of
+  // the LDS reads and of the dequantization, so that they issue while the
+  // matrix core works instead of in separate phases.
+#define SQ_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+#pragma unroll 1
+  for (int64_t kt = 0; kt < KT; ++kt) {
+    const bool aodd = kt & 1;
+    const uint8_t* acur = aodd ? big_a1 : big_a0;
+    // half-step 0: MFMAs of (kt, 0); read A of (kt, 1); dequantize B of (kt, 1)
+    read_a(af1, acur, 1);
+    mfma_step(af0, bj0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bj1[j] = dequant8_f16(bw1[j], bsc[j]);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      SQ_GROUP(0x008, 1);
+      SQ_GROUP(0x100, 1);
+      SQ_GROUP(0x008, 1);
+      SQ_GROUP(0x002, 4);
+      SQ_GROUP(0x008, 1);
+      SQ_GROUP(0x002, 4);
+      SQ_GROUP(0x008, 1);
+    }
+    // barrier: stage kt+1 has landed everywhere, buffer of stage kt is free
+    sync();
+    {
+      const int64_t kn = min(kt + 1, KT - 1);
+      const int64_t ssn = kn >> 2;
+      const int64_t ss = (kt + 5) >> 2;
+      u32x2 bw[FN];
+      // refill: A of stage kt+2 into this stage's buffer; quarter (kt+5) % 4 of
+      // super-stage (kt+5) / 4 of B (a super-stage ss is complete by the
+      // barrier of stage 4 ss - 1, whose second half-step reads it first)
+      a_issue(min(kt + 2, KT - 1), aodd ? big_a1 : big_a0);
+      bq_issue(min(ss, NSS - 1), (int)((kt + 5) & 3), (ss & 1) ? big_b1 : big_b0,
+               (ss & 1) ? big_s1 : big_s0);
+      // half-step 1: MFMAs of (kt, 1); read A and B of stage kt+1; dequantize (kt+1, 0)
+      read_b(bw, bsc, (ssn & 1) ? big_b1 : big_b0, (ssn & 1) ? big_s1 : big_s0, (int)(kn & 3));
+      read_a(af0, aodd ? big_a0 : big_a1, 0);
+      mfma_step(af1, bj1);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        bj0[j] = dequant8_f16(bw[j][0], bsc[j]);
+        bw1[j] = bw[j][1];
+      }
+      SQ_GROUP(0x020, 6);
+      SQ_GROUP(0x100, 8);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        SQ_GROUP(0x008, 1);
+        SQ_GROUP(0x100, 1);
+        SQ_GROUP(0x008, 1);
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        SQ_GROUP(0x008, 1);
+        SQ_GROUP(0x002, 4);
+        SQ_GROUP(0x008, 1);
+        SQ_GROUP(0x002, 4);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#undef SQ_GROUP
+
+  const int64_t rbase = m0 + 128 * wm, cbase = n0 + 64 * wn;
   // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA into the same accumulators
   for (int rr = 0; rr < rank; rr += 32) {
 #pragma unroll
@@ -651,8 +717,8 @@ __global__ void __launch_bounds__(128 * WNW, 1) k_fwd_gemm_big(
   const int lr4 = 4 * g;
   if (y_bf16) {
     // Each wave stages its 128 x 64 bf16 sub-tile (16 KB, 128-byte rows with
-    // the same chunk swizzle) in one half of a pipeline buffer, then stores
-    // eight whole 128-byte row segments per instruction.
+    // the chunk swizzle) in half of a pipeline buffer, then stores eight whole
+    // 128-byte row segments per instruction.
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // the final (unused) prefetches have landed
     __syncthreads();                        // every wave is done with the pipeline buffers
     const int wb = wave >> 1;
@@ -675,7 +741,7 @@ __global__ void __launch_bounds__(128 * WNW, 1) k_fwd_gemm_big(
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     __builtin_amdgcn_wave_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const bool full_cols = (cbase + WTN <= n) && ((n & 7) == 0);
+    const bool full_cols = (cbase + 64 <= n) && ((n & 7) == 0);
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
       const int lrow = 8 * it + (lane >> 3), chunk = lane & 7;
@@ -727,15 +793,15 @@ __global__ void __launch_bounds__(256) k_fwd_reduce(const float* __restrict__ pa
 // ---------------------------------------------------------------- host side
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Tile choice: the 256x256 tile (four 128x128 waves) when it yields enough
-// workgroups to cover the chip, else 128x128 with split-K.
+// Tile choice: the 256 x 256 tile when it yields at least half a tile per
+// CU, else 128 x 128 with split-K.
 FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   FwdPlan p{};
   p.m = m; p.n = n; p.k = k; p.group = group; p.rank = rank;
   const int64_t KT = k / GBK;
-  const int64_t big_tiles = ((m + 255) / 256) * ((n + 255) / 256);
-  if (big_tiles >= 512) {
-    p.tile_m = 256; p.tile_n = 256; p.splits = 1;
+  const int64_t big_tiles = ((m + BIG_BM - 1) / BIG_BM) * ((n + BIG_BN - 1) / BIG_BN);
+  if (big_tiles >= 128) {
+    p.tile_m = BIG_BM; p.tile_n = BIG_BN; p.splits = 1;
   } else {
     p.tile_m = 128; p.tile_n = 128;
     const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
@@ -791,13 +857,13 @@ hipError_t launch_fwd_contract(const FwdPlan& p, const uint8_t* codes, const uin
   hipError_t err;
   const int64_t tiles = ((p.m + p.tile_m - 1) / p.tile_m) * ((p.n + p.tile_n - 1) / p.tile_n);
   dim3 grid((unsigned)tiles, (unsigned)p.splits);
-  if (p.tile_m == 256) {
+  if (p.tile_n == BIG_BN) {
     if (p.group == 32)
-      hipLaunchKernelGGL(k_fwd_gemm_big<5>, dim3((unsigned)tiles), dim3(128 * BIG_WNW), 0, stream,
+      hipLaunchKernelGGL(k_fwd_gemm_big<5>, dim3((unsigned)tiles), dim3(BIG_THREADS), 0, stream,
                          b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k,
                          p.rank, y_bf16);
     else
-      hipLaunchKernelGGL(k_fwd_gemm_big<6>, dim3((unsigned)tiles), dim3(128 * BIG_WNW), 0, stream,
+      hipLaunchKernelGGL(k_fwd_gemm_big<6>, dim3((unsigned)tiles), dim3(BIG_THREADS), 0, stream,
                          b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k,
                          p.rank, y_bf16);
   } else {
