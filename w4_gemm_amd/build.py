@@ -27,9 +27,17 @@ FLAGS = [
 ]
 
 
+# Per-source extras.  The reconstruct kernel feeds its fp32 butterfly results
+# straight into MFMA accumulators; without this the register allocator routes
+# them through AGPRs (two extra moves per element).
+EXTRA = {
+    "sq_reconstruct.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -26,8 +26,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> one word of two bf16 (lo in the low half), round to nearest
+// even, in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float fp16_bits_to_f32(uint32_t bits16) {
@@ -70,6 +75,40 @@ __device__ __forceinline__ void fwht_cross64(float (&v)[64], int lane) {
   for (int i = 0; i < 64; ++i) {
     float p = __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v[i])));
     v[i] = __builtin_fmaf(s32, v[i], p);
+  }
+}
+
+// The same two stages with the gfx950 lane-swap instructions, which run on
+// the vector ALU instead of the LDS crossbar.  permlane16_swap(x, y)
+// exchanges the odd 16-lane rows of x with the even rows of y, so after it the
+// lanes of an even row hold (x, partner's x) and those of an odd row
+// (partner's y, y): one add and one subtract then finish the butterfly of
+// either element.  permlane32_swap does the same for the two 32-lane halves.
+// The result is not in the wave layout above: afterwards lane l (g = l/16)
+// holds, in register 32a + 16b + r (a, b in {0,1}, r < 16), block column
+//   swap_col(g, 32a + 16b + r) = 128b + 64a + 32(g & 1) + 16(g >> 1) + r,
+// that is four runs of 16 consecutive columns.
+__device__ __forceinline__ int swap_col(int g, int reg) {
+  return 128 * ((reg >> 4) & 1) + 64 * (reg >> 5) + 32 * (g & 1) + 16 * (g >> 1) + (reg & 15);
+}
+
+__device__ __forceinline__ void fwht_cross64_swap(float (&v)[64]) {
+#pragma unroll
+  for (int p = 0; p < 32; ++p) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[p]),
+                                                    __float_as_uint(v[p + 32]), false, false);
+    const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
+    v[p] = x + y;
+    v[p + 32] = x - y;
+  }
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    if (i & 16) continue;
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
+                                                    __float_as_uint(v[i + 16]), false, false);
+    const float x = __uint_as_float(r[0]), y = __uint_as_float(r[1]);
+    v[i] = x + y;
+    v[i + 16] = x - y;
   }
 }
 
