@@ -26,6 +26,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// Cache-policy operand of the gfx950 buffer intrinsics: non-temporal
+// (streaming) access.
+constexpr int SQ_CPOL_NT = 2;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
+// lgkmcnt [11:8]): wait for all vector memory operations, others untouched.
+constexpr int SQ_WAIT_VM0 = 0x0F70;
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 

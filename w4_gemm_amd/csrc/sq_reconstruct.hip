@@ -94,109 +94,140 @@ struct StripIn {
   uint32_t s2;   // fp16 bits: low half for columns 0..31 of the chunk, high for 32..63
 };
 
-// `cbase` / `sbase` point at the strip's first row and the block's first
-// column (wave-uniform); the lane offsets are 32-bit.
+// `cbase` / `sbase` point at the lane's row and the block's first column.
+// The loads are unconditional (callers clamp rows past the end to the last
+// row and never store those results): loads under divergent branches make
+// the compiler wait for every outstanding memory operation, stores included,
+// before the next strip.
+template <int GROUP>
 __device__ __forceinline__ void load_strip(StripIn& in, const uint8_t* cbase,
-                                           const uint16_t* sbase, bool live, uint32_t coff,
-                                           uint32_t soff, int group) {
-  if (live) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(cbase + coff);
-    in.w[0] = __builtin_nontemporal_load(src);
-    in.w[1] = __builtin_nontemporal_load(src + 1);
-    if (group == 32) {
-      in.s2 = *reinterpret_cast<const uint32_t*>(sbase + soff);
-    } else {
-      const uint32_t one = sbase[soff];
-      in.s2 = one | (one << 16);
-    }
+                                           const uint16_t* sbase, int g) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(cbase + 32 * g);
+  in.w[0] = __builtin_nontemporal_load(src);
+  in.w[1] = __builtin_nontemporal_load(src + 1);
+  if (GROUP == 32) {
+    in.s2 = *reinterpret_cast<const uint32_t*>(sbase + 2 * g);
   } else {
-    in.w[0] = in.w[1] = (u32x4){0u, 0u, 0u, 0u};
-    in.s2 = 0u;
+    in.s2 = sbase[g];
   }
 }
 
-template <int RANK>
+// Stores the staged 16 x 256 bf16 tile of strip row0: every instruction
+// writes two whole 512-byte row segments.  The buffer descriptor ends at the
+// last row of the weight, so rows of a ragged last strip are dropped by the
+// hardware range check instead of a branch (a branch around the stores
+// would make the compiler's wait counting assume the worst).
+__device__ __forceinline__ void store_tile(const u32x4* stage, uint16_t* w_hat, int64_t row0,
+                                           int64_t n, int64_t k, uint32_t stoff, int lane) {
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(w_hat + row0 * k), (short)0, (int)(min((int64_t)16, n - row0) * k * 2), 0x00020000);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 o = stage[(2 * j + (lane >> 5)) * STAGE_ROW_U4 + (lane & 31)];
+    __builtin_amdgcn_raw_buffer_store_b128(o, rsrc, stoff + (uint32_t)(4 * j) * (uint32_t)k, 0,
+                                           SQ_CPOL_NT);
+  }
+}
+
+template <int RANK, int GROUP>
 __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ up, const uint16_t* __restrict__ down,
-    uint16_t* __restrict__ w_hat, int64_t n, int64_t k, int group, int strips) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_stage[REC_WAVES][16][STAGE_ROW_U4 * 4];
+    uint16_t* __restrict__ w_hat, int64_t n, int64_t k, int strips) {
   constexpr int RC = RANK / 32;   // rank-32 chunks
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // A operands of the low-rank MFMA for the block, in fragment order
+  // [chunk][t][lane] so that every read is 64 consecutive 16-byte slots.
+  __shared__ u32x4 s_down[RC > 0 ? RC * 16 * 64 : 1];
+  // Per-wave output staging: 16 rows x 256 columns of bf16 (32 slots of
+  // 16 bytes) plus one pad slot per row.
+  __shared__ u32x4 s_stage[REC_WAVES][16 * STAGE_ROW_U4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nblk = k >> 8;
-  const int64_t wid = (int64_t)blockIdx.x * REC_WAVES + wave;
-  const int64_t blk = wid % nblk;
-  const int64_t run_row0 = (wid / nblk) * 16 * (int64_t)strips;
-  if (run_row0 >= n) return;
+  const int64_t nstr = (n + 15) / 16;
+  const int64_t blk = blockIdx.x % nblk;
+  const int64_t first = (int64_t)(blockIdx.x / nblk) * REC_WAVES * strips + wave;
   const int c = lane & 15, g = lane >> 4;
-  const int64_t spr = k / group;   // scales per row
-  // lane offsets within a strip (elements of each array)
-  const uint32_t coff = (uint32_t)(c * (k >> 1)) + 32u * g;
-  const uint32_t soff = (uint32_t)(c * spr) + (uint32_t)(64 * g / group);
-  const uint32_t uoff = (uint32_t)(c * RANK + 8 * g);
-  uint32_t stoff[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    stoff[j] = (uint32_t)((2 * j + (lane >> 5)) * k) + 8u * (lane & 31);
 
-  // A operand of the low-rank MFMA (row rho = c, k = r) for accumulator
-  // registers 4t .. 4t+3: the down row of the column that register 4t + c%4
-  // of lane group c/4 holds after the butterflies, so the product lands on
-  // the right columns (MFMA output row rho goes to lane group rho/4,
-  // register 4t + rho%4).
-  bf16x8 dfrag[RC > 0 ? RC : 1][16];
+  // Column of MFMA output row rho in accumulator register 4t + rho%4: the
+  // butterfly result that lane group rho/4 holds there (swap_col), so the
+  // product lands on the right columns.
+#pragma unroll
+  for (int m = 0; m < RC * 4; ++m) {
+    const int f = tid + 64 * REC_WAVES * m;
+    const int q = f >> 10, t = (f >> 6) & 15, l = f & 63;
+    const int64_t dcol = blk * 256 + swap_col((l & 15) >> 2, 4 * t + (l & 3));
+    s_down[f] = *reinterpret_cast<const u32x4*>(down + dcol * RANK + 32 * q + 8 * (l >> 4));
+  }
+  __syncthreads();
+  if (first >= nstr) return;
+
+  const int64_t spr = k / GROUP;   // scales per row
+  // byte offset of the lane's 16-byte store piece from the strip's first row
+  const uint32_t stoff = 2u * ((uint32_t)((lane >> 5) * k) + (uint32_t)(blk * 256) + 8u * (lane & 31));
+  const uint8_t* cblk = codes + blk * 128;
+  const uint16_t* sblk = scales + blk * (256 / GROUP);
+  u32x4* stage = &s_stage[wave][0];
+  // the lane's row of strip st, clamped to the last row
+  auto lrow = [&](int64_t st) { return min(st * 16 + c, n - 1); };
+
+  // This wave's strips: first, first + REC_WAVES, ... below nstr.
+  //
+  // Loads and stores share one in-order completion counter, and the
+  // compiler treats them as completing out of order, so a wait for a
+  // prefetched load also waits for every store issued before it.  Each
+  // iteration therefore starts with the wait, then issues the previous
+  // strip's stores (from LDS) and the next strip's loads back to back, and
+  // only then computes: the next wait is a whole strip of compute later.
+  const int cnt = (int)min((int64_t)strips, (nstr - first + REC_WAVES - 1) / REC_WAVES);
+  StripIn cur;
+  bf16x8 ufrag[RC > 0 ? RC : 1];
+  load_strip<GROUP>(cur, cblk + lrow(first) * (k >> 1), sblk + lrow(first) * spr, g);
 #pragma unroll
   for (int q = 0; q < RC; ++q)
+    ufrag[q] = *reinterpret_cast<const bf16x8*>(up + lrow(first) * RANK + 32 * q + 8 * g);
+
+  for (int i = 0; i < cnt; ++i) {
+    const int64_t st = first + (int64_t)REC_WAVES * i;
+    const int64_t row0 = st * 16;
+    __builtin_amdgcn_s_waitcnt(SQ_WAIT_VM0);
+    __builtin_amdgcn_sched_barrier(0);
+    // consume this strip's payload, then reuse its registers
+    const StripIn in = cur;
+    bf16x8 uf[RC > 0 ? RC : 1];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int64_t dcol = blk * 256 + swap_col(c >> 2, 4 * t + (c & 3));
-      dfrag[q][t] = *reinterpret_cast<const bf16x8*>(down + dcol * RANK + 32 * q + 8 * g);
+    for (int q = 0; q < RC; ++q) uf[q] = ufrag[q];
+    if (i > 0) store_tile(stage, w_hat, row0 - 16 * REC_WAVES, n, k, stoff, lane);
+    if (i + 1 < cnt) {
+      const int64_t nst = st + REC_WAVES;
+      load_strip<GROUP>(cur, cblk + lrow(nst) * (k >> 1), sblk + lrow(nst) * spr, g);
+#pragma unroll
+      for (int q = 0; q < RC; ++q)
+        ufrag[q] = *reinterpret_cast<const bf16x8*>(up + lrow(nst) * RANK + 32 * q + 8 * g);
     }
-
-  const int nstrip = (int)min((int64_t)strips, (n - run_row0 + 15) / 16);
-  StripIn cur;
-  load_strip(cur, codes + run_row0 * (k >> 1) + blk * 128, scales + run_row0 * spr + blk * 256 / group,
-             run_row0 + c < n, coff, soff, group);
-  u32x4* stage = reinterpret_cast<u32x4*>(&s_stage[wave][0][0]);
-
-  for (int s = 0; s < nstrip; ++s) {
-    const int64_t row0 = run_row0 + 16 * s;
-    const int64_t row = row0 + c;
-    const bool live = row < n;
-    // up fragment (B operand, k = r, col = output row c) and the next strip's codes
-    bf16x8 ufrag[RC > 0 ? RC : 1];
-#pragma unroll
-    for (int q = 0; q < RC; ++q)
-      ufrag[q] = live ? *reinterpret_cast<const bf16x8*>(up + row0 * RANK + uoff + 32 * q)
-                      : (bf16x8){};
-    StripIn nxt;
-    const bool more = s + 1 < nstrip;
-    if (more)
-      load_strip(nxt, codes + (row0 + 16) * (k >> 1) + blk * 128,
-                 scales + (row0 + 16) * spr + blk * 256 / group, row + 16 < n, coff, soff, group);
+    __builtin_amdgcn_sched_barrier(0);
 
     float v[64];
-    dequant_rotate64(v, cur.w, fp16_bits_to_f32(cur.s2 & 0xFFFFu) * 0.0625f,
-                     fp16_bits_to_f32(cur.s2 >> 16) * 0.0625f);
+    dequant_rotate64(v, in.w, fp16_bits_to_f32(in.s2 & 0xFFFFu) * 0.0625f,
+                     fp16_bits_to_f32(in.s2 >> 16) * 0.0625f);
     fwht_cross64_swap(v);
 #pragma unroll
     for (int q = 0; q < RC; ++q)
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, s_down[(q * 16 + t) * 64 + lane]);
         f32x4 acc = {v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dfrag[q][t], ufrag[q], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, uf[q], acc, 0, 0, 0);
         v[4 * t] = acc[0];
         v[4 * t + 1] = acc[1];
         v[4 * t + 2] = acc[2];
         v[4 * t + 3] = acc[3];
       }
 
-    // Transpose the 16 x 256 bf16 tile through LDS: lane (c, g) writes its
-    // 128 bytes (eight runs of 8 columns, placed by swap_col), then each
-    // store instruction takes two whole rows.  The wave's reads of the
-    // previous strip finished before its writes here (the stores consumed
-    // them), so only compiler ordering is needed.
+    // Stage the tile in LDS: lane (c, g) writes its eight runs of 8 columns
+    // (placed by swap_col).  The next iteration reads it back for the
+    // stores; LDS accesses of one wave complete in order.
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       u32x4 o;
@@ -206,46 +237,44 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
     }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rr = 2 * j + (lane >> 5), piece = lane & 31;
-      const u32x4 o = stage[rr * STAGE_ROW_U4 + piece];
-      if (row0 + rr < n)
-        __builtin_nontemporal_store(
-            o, reinterpret_cast<u32x4*>(w_hat + row0 * k + blk * 256 + stoff[j]));
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_wave_barrier();
-    if (more) cur = nxt;
   }
+  store_tile(stage, w_hat, (first + (int64_t)REC_WAVES * (cnt - 1)) * 16, n, k, stoff, lane);
 }
 
-// Strips per wave: enough waves to cover the chip a few times over, as few
-// factor reloads as that allows.
-int rec_strips_per_wave(int64_t n, int64_t k) {
-  const int64_t strips = (n + 15) / 16, nblk = k >> 8;
+// Strips per wave: as many as still leave a few workgroups per CU slot, so
+// that the block's factor is loaded as few times as that allows.
+static int rec_strips_per_wave(int64_t n, int64_t k) {
+  const int64_t nstr = (n + 15) / 16, nblk = k >> 8;
   int s = 8;
-  while (s > 1 && ((strips + s - 1) / s) * nblk < 4 * 256 * 4) s >>= 1;
+  while (s > 1 && ((nstr + REC_WAVES * s - 1) / (REC_WAVES * s)) * nblk < 3 * 4 * 256) s >>= 1;
   return s;
+}
+
+template <int RANK>
+static void launch_rank(dim3 grid, int group, hipStream_t stream, const uint8_t* codes,
+                        const uint16_t* scales, const uint16_t* up, const uint16_t* down,
+                        uint16_t* w_hat, int64_t n, int64_t k, int s) {
+  if (group == 32)
+    hipLaunchKernelGGL((k_reconstruct<RANK, 32>), grid, dim3(64 * REC_WAVES), 0, stream, codes,
+                       scales, up, down, w_hat, n, k, s);
+  else
+    hipLaunchKernelGGL((k_reconstruct<RANK, 64>), grid, dim3(64 * REC_WAVES), 0, stream, codes,
+                       scales, up, down, w_hat, n, k, s);
 }
 
 hipError_t launch_reconstruct(const uint8_t* codes, const uint16_t* scales, const uint16_t* up,
                               const uint16_t* down, uint16_t* w_hat, int64_t n, int64_t k,
                               int group, int rank, hipStream_t stream) {
-  const int64_t nblk = k >> 8;
+  const int64_t nblk = k >> 8, nstr = (n + 15) / 16;
   const int s = rec_strips_per_wave(n, k);
-  const int64_t runs = ((n + 15) / 16 + s - 1) / s;
-  const int64_t waves = runs * nblk;
-  dim3 grid((unsigned)((waves + REC_WAVES - 1) / REC_WAVES));
+  const int64_t runs = (nstr + REC_WAVES * s - 1) / (REC_WAVES * s);
+  dim3 grid((unsigned)(runs * nblk));
   if (rank == 0)
-    hipLaunchKernelGGL(k_reconstruct<0>, grid, dim3(64 * REC_WAVES), 0, stream, codes, scales, up,
-                       down, w_hat, n, k, group, s);
+    launch_rank<0>(grid, group, stream, codes, scales, up, down, w_hat, n, k, s);
   else if (rank == 32)
-    hipLaunchKernelGGL(k_reconstruct<32>, grid, dim3(64 * REC_WAVES), 0, stream, codes, scales, up,
-                       down, w_hat, n, k, group, s);
+    launch_rank<32>(grid, group, stream, codes, scales, up, down, w_hat, n, k, s);
   else
-    hipLaunchKernelGGL(k_reconstruct<64>, grid, dim3(64 * REC_WAVES), 0, stream, codes, scales, up,
-                       down, w_hat, n, k, group, s);
+    launch_rank<64>(grid, group, stream, codes, scales, up, down, w_hat, n, k, s);
   return hipGetLastError();
 }
 
