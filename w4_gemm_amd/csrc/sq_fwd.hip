@@ -5,15 +5,18 @@
 //   y[m][n] = 2^(E_m - 11) * ( sum_k xh16[m][k] * fp16(q[n][k] s[n][k/G])
 //                              + sum_r t16[m][r] * up[n][r] )
 //
-// Three launches on the caller's stream:
+// Four launches on the caller's stream:
 //   1. k_transpose_down: down [K][r] -> downT [r][K] (tiny; lets the MFMA
 //      operands of x @ down be read as 16-byte rows).
-//   2. k_fwd_pre: per 16 rows, (a) t = x @ down on bf16 MFMA and the row
-//      absmax A_m; E_m = ceil(log2 A_m); (b) xh = (x H) * 2^(11-E_m) with the
-//      256-point butterflies in registers/lanes, rounded to fp16 (|xh| <= 2^15
-//      because every entry of x H is at most 16 A_m), and t * 2^(11-E_m) split
-//      into bf16 hi + lo.
-//   3. k_fwd_gemm: the int4 contraction on fp16 MFMA.  The packed codes stream
+//   2. k_fwd_stats: per 16 rows and one slice of K, the partial row absmax
+//      and the partial t = x @ down on bf16 MFMA (one read of x).
+//   3. k_fwd_rotate: per 16 rows x one 256-column block, E_m = ceil(log2 A_m)
+//      from the slices' maxima and xh = (x H) * 2^(11-E_m) with the 256-point
+//      butterflies in registers and lane swaps, rounded to fp16 (|xh| <= 2^15
+//      because every entry of x H is at most 16 A_m) and stored through an
+//      LDS transpose; the first column group also adds the slices of t in a
+//      fixed order and splits t * 2^(11-E_m) into bf16 hi + lo.
+//   4. k_fwd_gemm: the int4 contraction on fp16 MFMA.  The packed codes stream
 //      from HBM as 16-byte loads, become fp16(q*s) in LDS (one rounding of the
 //      exact product), and meet the fp16 activations; the rank-r branch is two
 //      bf16 MFMA passes (hi and lo) into the same accumulators; the epilogue
@@ -44,136 +47,183 @@ __global__ void __launch_bounds__(256) k_transpose_down(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------- pre-phase
-constexpr int PRE_WAVES = 8;
+constexpr int PRE_WAVES = 4;
+constexpr int PRE_STAGE_U4 = 33;   // LDS staging row: 32 x 16 bytes + one pad slot
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ void load_x64(uint32_t (&xb)[32], const uint16_t* __restrict__ x,
-                                         int64_t row, bool live, int64_t k, int64_t col) {
-  if (live) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + row * k + col);
+// 64 consecutive bf16 of one row (128 bytes) as 32 words.
+__device__ __forceinline__ void load_x64(uint32_t (&xb)[32], const uint16_t* __restrict__ src) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 q = src[j];
-      xb[4 * j] = q[0];
-      xb[4 * j + 1] = q[1];
-      xb[4 * j + 2] = q[2];
-      xb[4 * j + 3] = q[3];
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 32; ++j) xb[j] = 0;
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 q = p[j];
+    xb[4 * j] = q[0];
+    xb[4 * j + 1] = q[1];
+    xb[4 * j + 2] = q[2];
+    xb[4 * j + 3] = q[3];
   }
 }
 
-__global__ void __launch_bounds__(512) k_fwd_pre(const uint16_t* __restrict__ x,
-                                                  const uint16_t* __restrict__ downT, int64_t m,
-                                                  int64_t k, int rank,
-                                                  uint16_t* __restrict__ xh,
-                                                  uint16_t* __restrict__ thi,
-                                                  uint16_t* __restrict__ tlo,
-                                                  float* __restrict__ rowscale) {
+// Smallest e with a <= 2^e for the bf16 magnitude bits `mx` (0 for a zero
+// row), floored at -100.
+__device__ __forceinline__ int row_exponent(uint32_t mx) {
+  const float a = bf16_to_f32(mx);
+  int e = 0;
+  if (a > 0.0f) {
+    int ex;
+    const float mant = frexpf(a, &ex);   // a = mant * 2^ex, mant in [0.5, 1)
+    e = (mant == 0.5f) ? ex - 1 : ex;
+  }
+  return max(e, -100);
+}
+
+// Pass 1: grid (ceil(m/16), slices); slice q covers the 256-column blocks
+// [q*bps, q*bps + bps) and the workgroup's four waves take every fourth one.
+// Writes amax_part[q][row] (bf16 magnitude bits; they order like the values)
+// and t_part[q][row][r] (fp32) for the rows below m.
+template <int RANK>
+__global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ downT, int64_t m, int64_t k,
+    int bps, uint32_t* __restrict__ amax_part, float* __restrict__ t_part) {
+  constexpr int RT = RANK / 16;   // 16-wide rank tiles
   __shared__ float red_t[PRE_WAVES][16][64];
   __shared__ uint32_t red_max[PRE_WAVES][64];
-  __shared__ float row_f[16];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
-  const int64_t row = row0 + c;
-  const bool live = row < m;
-  const int64_t nblk = k >> 8;
+  const int64_t lrow = min(row0 + c, m - 1);   // rows past m read the last row
+  const int64_t nblk = k >> 8, q = blockIdx.y;
+  const int64_t b_end = min(nblk, (q + 1) * bps);
 
-  // pass 1: t partial sums and |x| max (bf16 magnitudes compare as integers)
-  f32x4 acc[4] = {};
-  uint32_t amax = 0;
-  for (int64_t b = wave; b < nblk; b += PRE_WAVES) {
-    const int64_t col = b * 256 + 64 * g;
-    uint32_t xb[32];
-    load_x64(xb, x, row, live, k, col);
+  f32x4 acc[RT > 0 ? RT : 1] = {};
+  u16x2 amax2 = {0, 0};
+  for (int64_t b = q * bps + wave; b < b_end; b += PRE_WAVES) {
+    // MFMA j contracts columns 32j .. 32j+31 of the block; lane (c, g) holds
+    // eight of them, 32j + 8g .. +7, so the four lanes of a row read 64
+    // contiguous bytes (of x and of each downT row) per instruction.
+    const int64_t col = b * 256 + 8 * g;
+    u32x4 xv[8];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      amax = max(amax, xb[j] & 0x7FFFu);
-      amax = max(amax, (xb[j] >> 16) & 0x7FFFu);
-    }
+    for (int j = 0; j < 8; ++j) xv[j] = *reinterpret_cast<const u32x4*>(x + lrow * k + col + 32 * j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, xv[j][e] & 0x7FFF7FFFu));
+    // t: A = x (row c), B = downT (r = 16rt + c), both over the same columns
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      u32x4 araw = {xb[4 * j], xb[4 * j + 1], xb[4 * j + 2], xb[4 * j + 3]};
-      bf16x8 afrag = __builtin_bit_cast(bf16x8, araw);
+      const bf16x8 afrag = __builtin_bit_cast(bf16x8, xv[j]);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        if (16 * rt < rank) {
-          bf16x8 bfrag = *reinterpret_cast<const bf16x8*>(downT + (int64_t)(16 * rt + c) * k +
-                                                          col + 8 * j);
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag, acc[rt], 0, 0, 0);
-        }
+      for (int rt = 0; rt < RT; ++rt) {
+        const bf16x8 bfrag =
+            *reinterpret_cast<const bf16x8*>(downT + (int64_t)(16 * rt + c) * k + col + 32 * j);
+        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag, acc[rt], 0, 0, 0);
       }
     }
   }
   // acc[rt][i] = partial t[row0 + 4g + i][16 rt + c]
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-    if (16 * rt < rank)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red_t[wave][4 * g + i][16 * rt + c] = acc[rt][i];
-  red_max[wave][lane] = amax;
+    for (int i = 0; i < 4; ++i) red_t[wave][4 * g + i][16 * rt + c] = acc[rt][i];
+  red_max[wave][lane] = max((uint32_t)amax2[0], (uint32_t)amax2[1]);
   __syncthreads();
-  if (threadIdx.x < 16) {
-    const int rr = threadIdx.x;
-    uint32_t mx = 0;
-    for (int w = 0; w < PRE_WAVES; ++w)
-      for (int gg = 0; gg < 4; ++gg) mx = max(mx, red_max[w][rr + 16 * gg]);
-    const float a = bf16_to_f32(mx);
-    int e = 0;
-    if (a > 0.0f) {
-      int ex;
-      const float mant = frexpf(a, &ex);   // a = mant * 2^ex, mant in [0.5, 1)
-      e = (mant == 0.5f) ? ex - 1 : ex;    // smallest e with a <= 2^e
-    }
-    e = max(e, -100);
-    row_f[rr] = ldexpf(1.0f, 11 - e);
-    if (row0 + rr < m) rowscale[row0 + rr] = ldexpf(1.0f, e - 11);
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 16 * rank; i += 512) {
-    const int rr = i / rank, r = i - rr * rank;
+  for (int i = tid; i < 16 * RANK; i += 64 * PRE_WAVES) {
+    const int rr = i / RANK, r = i - rr * RANK;
     if (row0 + rr >= m) continue;
     float t = 0.0f;
+#pragma unroll
     for (int w = 0; w < PRE_WAVES; ++w) t += red_t[w][rr][r];
-    t *= row_f[rr];
-    const uint16_t hb = f32_to_bf16(t);
-    const uint16_t lb = f32_to_bf16(t - bf16_to_f32(hb));
-    thi[(row0 + rr) * rank + r] = hb;
-    tlo[(row0 + rr) * rank + r] = lb;
+    t_part[(q * m + row0 + rr) * RANK + r] = t;
   }
+  if (tid < 16 && row0 + tid < m) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int w = 0; w < PRE_WAVES; ++w)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) mx = max(mx, red_max[w][tid + 16 * gg]);
+    amax_part[q * m + row0 + tid] = mx;
+  }
+}
 
-  // pass 2: rotation, row scaling, fp16, permuted store
-  const float f = row_f[c] * 0.0625f;
-  for (int64_t b = wave; b < nblk; b += PRE_WAVES) {
-    const int64_t col = b * 256 + 64 * g;
-    uint32_t xb[32];
-    load_x64(xb, x, row, live, k, col);
-    float v[64];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      v[2 * j] = bf16_to_f32(xb[j] & 0xFFFFu);
-      v[2 * j + 1] = bf16_to_f32(xb[j] >> 16);
+// Pass 2: grid (ceil(m/16), ceil(nblk/4)); wave w of workgroup (i, j) owns
+// rows 16i.. and the 256-column block 4j + w.
+__global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
+    const uint16_t* __restrict__ x, int64_t m, int64_t k, int rank, int slices,
+    const uint32_t* __restrict__ amax_part, const float* __restrict__ t_part,
+    uint16_t* __restrict__ xh, uint16_t* __restrict__ thi, uint16_t* __restrict__ tlo,
+    float* __restrict__ rowscale) {
+  __shared__ u32x4 s_stage[PRE_WAVES][16 * PRE_STAGE_U4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t nblk = k >> 8;
+  auto exp_of = [&](int64_t row) {
+    uint32_t mx = 0;
+    for (int q = 0; q < slices; ++q) mx = max(mx, amax_part[q * m + row]);
+    return row_exponent(mx);
+  };
+
+  if (blockIdx.y == 0) {
+    // t slices in a fixed order, scaled, split into bf16 hi + lo
+    for (int i = tid; i < 16 * rank; i += 64 * PRE_WAVES) {
+      const int rr = i / rank, r = i - rr * rank;
+      const int64_t row = row0 + rr;
+      if (row >= m) continue;
+      float t = 0.0f;
+      for (int q = 0; q < slices; ++q) t += t_part[(q * m + row) * rank + r];
+      t *= ldexpf(1.0f, 11 - exp_of(row));
+      const uint16_t hb = f32_to_bf16(t);
+      thi[row * rank + r] = hb;
+      tlo[row * rank + r] = f32_to_bf16(t - bf16_to_f32(hb));
     }
-    fwht256_wave(v, lane);
-    if (live) {
-      u32x4 out[8];
+    if (tid < 16 && row0 + tid < m) rowscale[row0 + tid] = ldexpf(1.0f, exp_of(row0 + tid) - 11);
+  }
+  const int64_t b = (int64_t)blockIdx.y * PRE_WAVES + wave;
+  if (b >= nblk) return;
+
+  const int64_t lrow = min(row0 + c, m - 1);
+  const float f = ldexpf(1.0f, 11 - exp_of(lrow)) * 0.0625f;   // exact: a power of two
+  uint32_t xb[32];
+  load_x64(xb, x + lrow * k + b * 256 + 64 * g);
+  float v[64];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 32; ++j) {
+    v[2 * j] = bf16_to_f32(xb[j] & 0xFFFFu);
+    v[2 * j + 1] = bf16_to_f32(xb[j] >> 16);
+  }
+  fwht_inreg64(v);
+  fwht_cross64_swap(v);
+
+  // fp16 in the permuted K order: word p of each 8-column run holds columns
+  // p and p + 4; the run of registers 8j.. holds columns swap_col(g, 8j)..
+  u32x4* stage = &s_stage[wave][0];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const _Float16 lo = (_Float16)(v[8 * j + p] * f);
-          const _Float16 hi = (_Float16)(v[8 * j + p + 4] * f);
-          out[j][p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
-      }
-      u32x4* dst = reinterpret_cast<u32x4*>(xh + row * k + col);
+  for (int j = 0; j < 8; ++j) {
+    u32x4 o;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = out[j];
+    for (int p = 0; p < 4; ++p) {
+      const _Float16 lo = (_Float16)(v[8 * j + p] * f);
+      const _Float16 hi = (_Float16)(v[8 * j + p + 4] * f);
+      o[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
+    stage[c * PRE_STAGE_U4 + (swap_col(g, 8 * j) >> 3)] = o;
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+  // every store instruction writes two whole 512-byte row segments; the
+  // descriptor ends at row m, so rows of a ragged last strip are dropped
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(xh + row0 * k), (short)0, (int)(min((int64_t)16, m - row0) * k * 2), 0x00020000);
+  const uint32_t off = 2u * ((uint32_t)((lane >> 5) * k) + (uint32_t)(b * 256) + 8u * (lane & 31));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const u32x4 o = stage[(2 * j + (lane >> 5)) * PRE_STAGE_U4 + (lane & 31)];
+    __builtin_amdgcn_raw_buffer_store_b128(o, rsrc, off + (uint32_t)(4 * j) * (uint32_t)k, 0, 0);
   }
 }
 
@@ -815,6 +865,13 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   p.off_tlo = off;       off = align256(off + (size_t)m * std::max(rank, 1) * 2);
   p.off_rowscale = off;  off = align256(off + (size_t)m * 4);
   p.off_downT = off;     off = align256(off + (size_t)k * std::max(rank, 1) * 2);
+  // K slices of the statistics pass: two blocks per wave when that still
+  // leaves a thousand workgroups, else one
+  const int64_t strips = (m + 15) / 16, nblk = k / 256;
+  p.pre_bps = strips * ((nblk + 7) / 8) >= 1024 ? 8 : PRE_WAVES;
+  p.pre_slices = (int)((nblk + p.pre_bps - 1) / p.pre_bps);
+  p.off_amax = off;      off = align256(off + (size_t)p.pre_slices * m * 4);
+  p.off_tpart = off;     off = align256(off + (size_t)p.pre_slices * m * std::max(rank, 1) * 4);
   p.off_partial = off;   off = align256(off + (p.splits > 1 ? (size_t)p.splits * m * n * 4 : 0));
   p.total = off;
   return p;
@@ -823,6 +880,8 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
 struct FwdBuffers {
   uint16_t *xh, *thi, *tlo, *downT;
   float *rowscale, *partial;
+  uint32_t* amax;
+  float* tpart;
 };
 
 static FwdBuffers carve(const FwdPlan& p, void* workspace) {
@@ -832,7 +891,9 @@ static FwdBuffers carve(const FwdPlan& p, void* workspace) {
                     reinterpret_cast<uint16_t*>(ws + p.off_tlo),
                     reinterpret_cast<uint16_t*>(ws + p.off_downT),
                     reinterpret_cast<float*>(ws + p.off_rowscale),
-                    reinterpret_cast<float*>(ws + p.off_partial)};
+                    reinterpret_cast<float*>(ws + p.off_partial),
+                    reinterpret_cast<uint32_t*>(ws + p.off_amax),
+                    reinterpret_cast<float*>(ws + p.off_tpart)};
 }
 
 hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t* down,
@@ -845,8 +906,21 @@ hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t
                        down, b.downT, p.k, p.rank);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(k_fwd_pre, dim3((unsigned)((p.m + 15) / 16)), dim3(512), 0, stream, x,
-                     b.downT, p.m, p.k, p.rank, b.xh, b.thi, b.tlo, b.rowscale);
+  const unsigned strips = (unsigned)((p.m + 15) / 16);
+  const dim3 sgrid(strips, (unsigned)p.pre_slices);
+  if (p.rank == 0)
+    hipLaunchKernelGGL(k_fwd_stats<0>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m, p.k,
+                       p.pre_bps, b.amax, b.tpart);
+  else if (p.rank == 32)
+    hipLaunchKernelGGL(k_fwd_stats<32>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m,
+                       p.k, p.pre_bps, b.amax, b.tpart);
+  else
+    hipLaunchKernelGGL(k_fwd_stats<64>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m,
+                       p.k, p.pre_bps, b.amax, b.tpart);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_fwd_rotate, dim3(strips, (unsigned)((p.k / 256 + PRE_WAVES - 1) / PRE_WAVES)),
+                     dim3(64 * PRE_WAVES), 0, stream, x, p.m, p.k, p.rank, p.pre_slices, b.amax,
+                     b.tpart, b.xh, b.thi, b.tlo, b.rowscale);
   return hipGetLastError();
 }
 

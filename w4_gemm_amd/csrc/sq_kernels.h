@@ -19,7 +19,8 @@ struct FwdPlan {
   int group, rank;
   int splits;          // split-K factor of the main contraction
   int tile_m, tile_n;  // output tile of the main contraction
-  size_t off_xh, off_thi, off_tlo, off_rowscale, off_downT, off_partial, total;
+  int pre_bps, pre_slices;  // 256-column blocks per K slice of the statistics pass, slices
+  size_t off_xh, off_thi, off_tlo, off_rowscale, off_downT, off_amax, off_tpart, off_partial, total;
 };
 FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank);
 
