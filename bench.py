@@ -14,14 +14,25 @@ reads.  The headline `value` is the fused forward's TFLOP/s at
 GB/s are reported beside it.
 
 The `roofline` object is for the forward's dominant kernel (the contraction,
-k_fwd_gemm, timed alone through sq_linear_fwd_contract).  `cpu_baseline` is
-the CPU oracle's forward on a sample of rows, on this host's cores.
+k_fwd_gemm_big, timed alone through sq_linear_fwd_contract).  Its `traffic`
+is the HBM bytes per launch that rocprofv3 counters measured for that kernel
+(FETCH_SIZE + WRITE_SIZE, each scaled by the ratio of known bytes to counted
+bytes of a plain device copy), read from the committed counter summary under
+profiles/; it is null when the kernel source has changed since then.
+`cpu_baseline` is the CPU oracle's forward on a sample of rows, on this
+host's cores.
+
+Extra fields: the small-M forward sweep (M = 1, 16, 128 on the
+6144x16384 g32 weight) in GB/s of bytes the call must move, and the
+rotation, reconstruct and quantize kernels against HBM peak.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 4]
+       python bench.py --ops copy      (the counter calibration copy only)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +45,34 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+# counter summary of the contraction kernel at 4480x16384x6144 (see its header)
+GEMM_PMC = os.path.join(ROOT, "profiles", "k_fwd_gemm_big_mlp-up_4480x16384x6144_pmc.txt")
+GEMM_SRC = os.path.join(ROOT, "w4_gemm_amd", "csrc", "sq_fwd.hip")
+COPY_BYTES = 256 << 20        # calibration copy: 256 MiB read + 256 MiB written
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(path, src):
+    """HBM bytes per launch from a counter summary, or None if it is missing
+    or was taken on a different kernel source."""
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256_16") != source_sha(src):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -44,7 +83,8 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--ops", default="fwd,reconstruct,quantize")
+    ap.add_argument("--ops", default="fwd,reconstruct,quantize,smallm")
+    ap.add_argument("--small-m", default="1,16,128")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; the layer shards by output rows "
@@ -58,6 +98,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.ops == "copy":
+        return copy_calibration(torch, dev)
     cfg = CONFIGS[args.config]
     M, N, K, G, R = cfg.M, cfg.N, cfg.K, cfg.group, cfg.rank
     ops = args.ops.split(",")
@@ -143,6 +185,10 @@ def main():
             b.record()
         torch.cuda.synchronize()
         res["quantize"] = np.array([a.elapsed_time(b) for a, b in marks])
+    # ---------------------------------------------------------------- small-M sweep
+    if "smallm" in ops and args.small_m:
+        res["smallm"] = small_m_sweep(torch, W, dev, [int(v) for v in args.small_m.split(",")],
+                                      args.steps, args.warmup)
     torch.cuda.synchronize()
     wall = time.time() - t0
 
@@ -158,25 +204,34 @@ def main():
         tot, rot, con = res["fwd"]
         t_fwd, t_rot, t_con = float(np.mean(tot)), float(np.mean(rot)), float(np.mean(con))
         ms_step += t_fwd
-        out.update(fwd_ms=t_fwd, fwd_ms_p10=float(np.percentile(tot, 10)),
+        out.update(fwd_ms=t_fwd, fwd_ms_median=float(np.median(tot)),
+                   fwd_ms_p10=float(np.percentile(tot, 10)),
                    fwd_ms_p90=float(np.percentile(tot, 90)), fwd_rotate_ms=t_rot,
                    fwd_contract_ms=t_con, fwd_tflops=flops_fwd / (t_fwd * 1e-3) / 1e12)
         out["fwd_pct_bf16_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_F16_TFLOPS
+        # rotation half: reads x twice, writes xh (fp16); the t / stats side buffers are small
+        rot_bytes = 3.0 * M * K * 2
+        out["fwd_rotate_gbps"] = rot_bytes / (t_rot * 1e-3) / 1e9
         achieved = flops_gemm / (t_con * 1e-3) / 1e12
-        out["roofline"] = {"bound": "mfma", "kernel": "k_fwd_gemm", "achieved": achieved,
+        out["roofline"] = {"bound": "mfma", "kernel": "k_fwd_gemm_big", "achieved": achieved,
                            "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": achieved / PEAK_F16_TFLOPS, "traffic": None,
-                           "per_launch_flops": flops_gemm}
+                           "frac": achieved / PEAK_F16_TFLOPS,
+                           "traffic": measured_traffic(GEMM_PMC, GEMM_SRC),
+                           "per_launch_flops": flops_gemm,
+                           "algorithmic_bytes_per_launch": M * K * 2 + pay_bytes + M * N * 2}
     if "reconstruct" in res:
         t = float(np.mean(res["reconstruct"]))
         ms_step += t
-        out.update(reconstruct_ms=t, reconstruct_gbps=rec_bytes / (t * 1e-3) / 1e9)
+        out.update(reconstruct_ms=t, reconstruct_ms_median=float(np.median(res["reconstruct"])),
+                   reconstruct_gbps=rec_bytes / (t * 1e-3) / 1e9)
         out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
     if "quantize" in res:
         t = float(np.mean(res["quantize"]))
         ms_step += t
         out.update(quantize_ms=t, quantize_gbps=quant_bytes / (t * 1e-3) / 1e9)
         out["quantize_pct_hbm_peak"] = 100.0 * out["quantize_gbps"] / PEAK_HBM_GBPS
+    if "smallm" in res:
+        out["fwd_small_m"] = res["smallm"]
 
     line = {
         "metric": "fused W4 fwd TFLOP/s (% bf16 MFMA peak) at 4480x16384x6144; reconstruct GB/s",
@@ -205,6 +260,84 @@ def main():
         line["cpu_baseline"] = cpu_baseline(p0, x, cfg, args.cpu_rows)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def copy_calibration(torch, dev, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    n = COPY_BYTES // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t) / reps
+    print(json.dumps({"calibration_copy_bytes_read": COPY_BYTES, "calibration_copy_bytes_written":
+                      COPY_BYTES, "ms": dt * 1e3}), flush=True)
+    return 0
+
+
+def small_m_sweep(torch, W, dev, ms, steps, warmup):
+    """Forward at small M on the 6144x16384 g32 rank-32 weight, HBM-bound:
+    GB/s of the bytes one call must move (payload + x + y), first M rows of
+    the M=4480 activation draw.  At these sizes one call's kernels run for
+    less time than the host needs to enqueue them, so the calls are captured
+    once in a HIP graph and the graph is replayed: the figure is GPU time
+    per call (`us`), with the eager per-call time beside it (`eager_us`)."""
+    from synth import CONFIGS, gen_activations, gen_weight
+    cfg = CONFIGS[5]
+    N, K, G, R = cfg.N, cfg.K, cfg.group, cfg.rank
+    rng = np.random.default_rng(0)
+    w = torch.from_numpy(gen_weight(rng, N, K, cfg.spike)).to(dev)
+    x_all = gen_activations(rng, cfg.M, K, cfg.outlier_frac)
+    torch.manual_seed(0)
+    u, s, v = torch.svd_lowrank(w, q=R + 8, niter=2)
+    rs = s[:R].sqrt()
+    up = (u[:, :R] * rs).to(torch.bfloat16).contiguous()
+    down = (v[:, :R] * rs).to(torch.bfloat16).contiguous()
+    p, _, flags = W.quantize_weight(w, up, down, G)
+    torch.cuda.synchronize()
+    assert int(flags[0]) == 0
+    del w, u, v
+    pay = N * K / 2 + N * (K // G) * 2 + (N + K) * R * 2
+    out = {}
+    for m in ms:
+        x = torch.from_numpy(x_all[:m].view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(W.fwd_workspace_bytes(m, p), dtype=torch.uint8, device=dev)
+        for _ in range(warmup):
+            W.linear_fwd(x, p, out=y, workspace=ws)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            W.linear_fwd(x, p, out=y, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        eager = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        # graph: `steps` calls captured back to back on a side stream
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(steps):
+                    W.linear_fwd(x, p, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / steps
+        by = pay + m * K * 2 + m * N * 2
+        out[str(m)] = {"us": t * 1e3, "eager_us": eager * 1e3, "gbps": by / (t * 1e-3) / 1e9,
+                       "pct_hbm_peak": 100.0 * by / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                       "tflops": (2.0 * m * N * K + 2.0 * m * R * (N + K)) / (t * 1e-3) / 1e12}
+    return out
 
 
 def cpu_baseline(p, x, cfg, rows):

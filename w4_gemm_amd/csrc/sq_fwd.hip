@@ -156,16 +156,20 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
     uint16_t* __restrict__ xh, uint16_t* __restrict__ thi, uint16_t* __restrict__ tlo,
     float* __restrict__ rowscale) {
   __shared__ u32x4 s_stage[PRE_WAVES][16 * PRE_STAGE_U4];
+  __shared__ int s_exp[16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   const int64_t nblk = k >> 8;
-  auto exp_of = [&](int64_t row) {
+  // E of the workgroup's rows (rows past m repeat the last row)
+  if (tid < 16) {
+    const int64_t row = min(row0 + tid, m - 1);
     uint32_t mx = 0;
     for (int q = 0; q < slices; ++q) mx = max(mx, amax_part[q * m + row]);
-    return row_exponent(mx);
-  };
+    s_exp[tid] = row_exponent(mx);
+  }
+  __syncthreads();
 
   if (blockIdx.y == 0) {
     // t slices in a fixed order, scaled, split into bf16 hi + lo
@@ -174,19 +178,27 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
       const int64_t row = row0 + rr;
       if (row >= m) continue;
       float t = 0.0f;
-      for (int q = 0; q < slices; ++q) t += t_part[(q * m + row) * rank + r];
-      t *= ldexpf(1.0f, 11 - exp_of(row));
+      int q = 0;
+      for (; q + 4 <= slices; q += 4) {
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = t_part[((q + u) * m + row) * rank + r];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t += v[u];
+      }
+      for (; q < slices; ++q) t += t_part[(q * m + row) * rank + r];
+      t *= ldexpf(1.0f, 11 - s_exp[rr]);
       const uint16_t hb = f32_to_bf16(t);
       thi[row * rank + r] = hb;
       tlo[row * rank + r] = f32_to_bf16(t - bf16_to_f32(hb));
     }
-    if (tid < 16 && row0 + tid < m) rowscale[row0 + tid] = ldexpf(1.0f, exp_of(row0 + tid) - 11);
+    if (tid < 16 && row0 + tid < m) rowscale[row0 + tid] = ldexpf(1.0f, s_exp[tid] - 11);
   }
   const int64_t b = (int64_t)blockIdx.y * PRE_WAVES + wave;
   if (b >= nblk) return;
 
   const int64_t lrow = min(row0 + c, m - 1);
-  const float f = ldexpf(1.0f, 11 - exp_of(lrow)) * 0.0625f;   // exact: a power of two
+  const float f = ldexpf(1.0f, 11 - s_exp[c]) * 0.0625f;   // exact: a power of two
   uint32_t xb[32];
   load_x64(xb, x + lrow * k + b * 256 + 64 * g);
   float v[64];
@@ -824,6 +836,150 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
   }
 }
 
+// ---------------------------------------------------------------- small M
+// For M <= 64 the contraction is a stream of the payload past a few rows of
+// activations.  One wave owns 64 weight rows and one K slice: per 128 K
+// values it loads 16 bytes of codes per lane and weight-row tile (the
+// next chunk's codes are in flight while this one computes), dequantizes them
+// once into MFMA B fragments and reuses those for every 16-row tile of x.
+// MFMA step e of a chunk contracts K offsets 32g + 8e .. +7 in lane group g,
+// so one lane's 16 code bytes and 64 activation bytes are contiguous; both
+// operands keep the permuted order inside each group of 8.  Rows of xh past
+// M and weight rows past N come back as zeros from range-checked buffer
+// loads.  Split-K partials go to the workspace (fixed-order sum in
+// k_fwd_reduce); split 0 also adds the rank-r branch.
+constexpr int SK_ROWS = 64;
+
+template <int GSHIFT, int MT>
+__global__ void __launch_bounds__(64) k_fwd_skinny(
+    const uint16_t* __restrict__ xh, const uint8_t* __restrict__ codes,
+    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
+    const uint16_t* __restrict__ tlo, const uint16_t* __restrict__ up,
+    float* __restrict__ partial, int64_t m, int64_t n, int64_t k, int rank, int kslice) {
+  const int lane = threadIdx.x, fr = lane & 15, g = lane >> 4;
+  // K slice fastest: neighbouring workgroups sweep whole weight rows
+  const int64_t n0 = (int64_t)blockIdx.y * SK_ROWS;
+  const int ks = blockIdx.x;
+  const int64_t k0 = (int64_t)ks * kslice, k1 = min(k, k0 + kslice);
+  const int64_t half_k = k >> 1, ngroups = k >> GSHIFT;
+  const int64_t b_rows = min((int64_t)SK_ROWS, n - n0);
+  const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(codes + n0 * half_k), (short)0, (int)(b_rows * half_k), 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scales + n0 * ngroups), (short)0, (int)(b_rows * ngroups * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)xh, (short)0, (int)(m * k * 2), 0x00020000);
+  // byte offsets at K offset 0
+  uint32_t c_off[4], s_off[4], a_off[MT];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    c_off[t] = (uint32_t)((16 * t + fr) * half_k) + 16u * g;
+    s_off[t] = (uint32_t)((16 * t + fr) * ngroups) * 2u;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) a_off[mt] = (uint32_t)((16 * mt + fr) * k + 32 * g) * 2u;
+
+  // kb < 0 asks for nothing: the offsets land past the descriptors' range,
+  // so the loads return zeros without touching memory (no branch, so the
+  // compiler's wait counting stays exact)
+  auto load_codes = [&](u32x4 (&cw)[4], uint32_t (&sc)[4], int64_t kb) {
+    const uint32_t off = kb < 0 ? 0x80000000u : 0u;
+    kb = kb < 0 ? 0 : kb;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      cw[t] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off + c_off[t] + (uint32_t)(kb >> 1), 0,
+                                                    SQ_CPOL_NT);
+      sc[t] = __builtin_amdgcn_raw_buffer_load_b16(
+          s_rsrc, off + s_off[t] + (uint32_t)(((kb + 32 * g) >> GSHIFT) * 2), 0, 0);
+    }
+  };
+
+  f32x4 acc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[mt][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // One chunk: activations first, then the codes of the chunk after next
+  // into the registers the previous chunk used (loads complete in order, so
+  // waiting for the activations leaves that prefetch in flight); two
+  // register sets alternate, so no copy forces an early wait.
+  auto chunk = [&](const u32x4 (&cw)[4], const uint32_t (&sc)[4], u32x4 (&cn)[4],
+                   uint32_t (&sn)[4], int64_t kb, int64_t kpre) {
+    half8 af[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        af[mt][e] = __builtin_bit_cast(
+            half8, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, a_off[mt] + (uint32_t)((kb + 8 * e) * 2),
+                                                         0, 0));
+    half8 bf[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sc[t]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bf[t][e] = dequant8_f16(cw[t][e], sv);
+    }
+    load_codes(cn, sn, kpre);
+    __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt][e], bf[t][e], acc[mt][t], 0, 0, 0);
+  };
+  // the slice is a whole number of 256-value pairs of chunks
+  u32x4 cw0[4], cw1[4];
+  uint32_t sc0[4], sc1[4];
+  load_codes(cw0, sc0, k0);
+  __builtin_amdgcn_sched_barrier(0);   // chunk 0's codes are issued first
+  load_codes(cw1, sc1, k0 + 128);
+  for (int64_t kb = k0; kb < k1; kb += 256) {
+    const bool more = kb + 256 < k1;
+    chunk(cw0, sc0, cw0, sc0, kb, more ? kb + 256 : -1);
+    chunk(cw1, sc1, cw1, sc1, kb + 128, more ? kb + 384 : -1);
+  }
+
+  if (ks == 0) {
+    // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA
+    for (int rr = 0; rr < rank; rr += 32) {
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl) {
+        const uint16_t* tsrc = hl ? tlo : thi;
+        bf16x8 bu[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int64_t c = min(n0 + 16 * t + fr, n - 1);
+          bu[t] = *reinterpret_cast<const bf16x8*>(up + c * rank + rr + 8 * g);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int64_t r = min((int64_t)(16 * mt + fr), m - 1);
+          const bf16x8 at = *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + 8 * g);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at, bu[t], acc[mt][t], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // acc[mt][t][i]: row 16 mt + 4g + i, column n0 + 16 t + fr
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = 16 * mt + 4 * g + i;
+      if (r >= m) continue;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t c = n0 + 16 * t + fr;
+        if (c < n) partial[((int64_t)ks * m + r) * n + c] = acc[mt][t][i];
+      }
+    }
+}
+
 // ---------------------------------------------------------------- split-K sum
 __global__ void __launch_bounds__(256) k_fwd_reduce(const float* __restrict__ partial,
                                                      const float* __restrict__ rowscale,
@@ -831,8 +987,18 @@ __global__ void __launch_bounds__(256) k_fwd_reduce(const float* __restrict__ pa
                                                      int splits, int y_bf16) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= m * n) return;
+  // fixed summation order; the loads of a group of eight are all in flight
   float s = 0.0f;
-  for (int z = 0; z < splits; ++z) s += partial[(int64_t)z * m * n + i];   // fixed order
+  const int64_t mn = m * n;
+  int z = 0;
+  for (; z + 8 <= splits; z += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[(int64_t)(z + u) * mn + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; z < splits; ++z) s += partial[(int64_t)z * mn + i];
   s *= rowscale[i / n];
   if (y_bf16)
     reinterpret_cast<uint16_t*>(y)[i] = f32_to_bf16(s);
@@ -850,7 +1016,25 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   p.m = m; p.n = n; p.k = k; p.group = group; p.rank = rank;
   const int64_t KT = k / GBK;
   const int64_t big_tiles = ((m + BIG_BM - 1) / BIG_BM) * ((n + BIG_BN - 1) / BIG_BN);
-  if (big_tiles >= 128) {
+  p.skinny_mt = 0;
+  if (m <= 64) {
+    // small M: 16-row tiles rounded up to 1, 2 or 4; split K into slices
+    // for about a thousand waves (long slices stream best: each wave keeps
+    // one 256-value step of codes in flight) while the fp32 partials stay
+    // under ~15 % of the payload bytes
+    p.skinny_mt = m <= 16 ? 1 : m <= 32 ? 2 : 4;
+    const int64_t ntiles = (n + SK_ROWS - 1) / SK_ROWS;
+    const double pay = (double)n * k * (0.5 + 2.0 / group);
+    int64_t s = (1024 + ntiles - 1) / ntiles;
+    s = std::min<int64_t>(s, std::max<int64_t>(1, (int64_t)(0.15 * pay / (4.0 * m * n))));
+    s = std::max<int64_t>(1, s);
+    const int64_t chunks = k / 256;
+    s = std::min<int64_t>(s, chunks);
+    const int64_t per = (chunks + s - 1) / s;
+    p.skinny_kslice = (int)(per * 256);
+    p.splits = (int)((chunks + per - 1) / per);
+    p.tile_m = 16 * p.skinny_mt; p.tile_n = SK_ROWS;
+  } else if (big_tiles >= 128) {
     p.tile_m = BIG_BM; p.tile_n = BIG_BN; p.splits = 1;
   } else {
     p.tile_m = 128; p.tile_n = 128;
@@ -872,7 +1056,8 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   p.pre_slices = (int)((nblk + p.pre_bps - 1) / p.pre_bps);
   p.off_amax = off;      off = align256(off + (size_t)p.pre_slices * m * 4);
   p.off_tpart = off;     off = align256(off + (size_t)p.pre_slices * m * std::max(rank, 1) * 4);
-  p.off_partial = off;   off = align256(off + (p.splits > 1 ? (size_t)p.splits * m * n * 4 : 0));
+  const bool partials = p.splits > 1 || p.skinny_mt > 0;
+  p.off_partial = off;   off = align256(off + (partials ? (size_t)p.splits * m * n * 4 : 0));
   p.total = off;
   return p;
 }
@@ -931,7 +1116,18 @@ hipError_t launch_fwd_contract(const FwdPlan& p, const uint8_t* codes, const uin
   hipError_t err;
   const int64_t tiles = ((p.m + p.tile_m - 1) / p.tile_m) * ((p.n + p.tile_n - 1) / p.tile_n);
   dim3 grid((unsigned)tiles, (unsigned)p.splits);
-  if (p.tile_n == BIG_BN) {
+  if (p.skinny_mt > 0) {
+    const dim3 sg((unsigned)p.splits, (unsigned)((p.n + SK_ROWS - 1) / SK_ROWS));
+#define SQ_SKINNY(GS, MT)                                                                         \
+  hipLaunchKernelGGL((k_fwd_skinny<GS, MT>), sg, dim3(64), 0, stream, b.xh, codes, scales, b.thi, \
+                     b.tlo, up, b.partial, p.m, p.n, p.k, p.rank, p.skinny_kslice)
+    if (p.group == 32) {
+      if (p.skinny_mt == 1) SQ_SKINNY(5, 1); else if (p.skinny_mt == 2) SQ_SKINNY(5, 2); else SQ_SKINNY(5, 4);
+    } else {
+      if (p.skinny_mt == 1) SQ_SKINNY(6, 1); else if (p.skinny_mt == 2) SQ_SKINNY(6, 2); else SQ_SKINNY(6, 4);
+    }
+#undef SQ_SKINNY
+  } else if (p.tile_n == BIG_BN) {
     if (p.group == 32)
       hipLaunchKernelGGL(k_fwd_gemm_big<5>, dim3((unsigned)tiles), dim3(BIG_THREADS), 0, stream,
                          b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k,
@@ -946,7 +1142,7 @@ hipError_t launch_fwd_contract(const FwdPlan& p, const uint8_t* codes, const uin
                        p.k, p.group, p.rank, p.splits, y_bf16);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (p.splits > 1) {
+  if (p.splits > 1 || p.skinny_mt > 0) {
     const int64_t cnt = p.m * p.n;
     hipLaunchKernelGGL(k_fwd_reduce, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
                        b.partial, b.rowscale, y, p.m, p.n, p.splits, y_bf16);

@@ -19,6 +19,8 @@ struct FwdPlan {
   int group, rank;
   int splits;          // split-K factor of the main contraction
   int tile_m, tile_n;  // output tile of the main contraction
+  int skinny_mt;       // > 0: the small-M kernel with this many 16-row tiles
+  int skinny_kslice;   // its K slice (a multiple of 256)
   int pre_bps, pre_slices;  // 256-column blocks per K slice of the statistics pass, slices
   size_t off_xh, off_thi, off_tlo, off_rowscale, off_downT, off_amax, off_tpart, off_partial, total;
 };
