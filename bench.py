@@ -263,7 +263,10 @@ def main():
 
 
 def copy_calibration(torch, dev, reps=5):
-    """A plain device copy of known size, for scaling the HBM byte counters."""
+    """Plain device copies of known size, for scaling the HBM byte counters:
+    torch's copy_ (the runtime's blit kernel) and an elementwise kernel
+    (b = a * 1, vector loads and stores like the library's kernels), each
+    reading COPY_BYTES and writing COPY_BYTES."""
     n = COPY_BYTES // 4
     a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
     b = torch.empty_like(a)
@@ -273,8 +276,13 @@ def copy_calibration(torch, dev, reps=5):
         b.copy_(a)
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t) / reps
+    t = time.perf_counter()
+    for _ in range(reps):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    dt2 = (time.perf_counter() - t) / reps
     print(json.dumps({"calibration_copy_bytes_read": COPY_BYTES, "calibration_copy_bytes_written":
-                      COPY_BYTES, "ms": dt * 1e3}), flush=True)
+                      COPY_BYTES, "blit_ms": dt * 1e3, "elementwise_ms": dt2 * 1e3}), flush=True)
     return 0
 
 
