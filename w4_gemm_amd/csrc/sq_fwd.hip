@@ -547,22 +547,29 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0], expcnt [6:4], lgkmcnt [11:8])
 constexpr int WAIT_VM0 = 0x0F70, WAIT_LGKM0 = 0xC07F;
 
-template <int GSHIFT>   // log2 of the group size
+// BM: tile rows, 256 or 224 (the LDS A tile always has 256 rows; with 224 the
+// last 32 load a clamped row and are not read).  plan_fwd picks the height
+// that needs the fewest tile-rounds of the chip, so that M = 4480 fills five
+// whole rounds of 224-row tiles instead of 4.5 rounds of 256-row tiles.
+template <int GSHIFT, int BM>   // log2 of the group size, tile rows
 __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     const uint16_t* __restrict__ xh, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
     const uint16_t* __restrict__ tlo, const uint16_t* __restrict__ up,
     const float* __restrict__ rowscale, void* __restrict__ y, int64_t m, int64_t n, int64_t k,
     int rank, int y_bf16) {
-  constexpr int FN = 4;   // wave tile 128 x 64
+  static_assert(BM == 256 || BM == 224, "tile rows");
+  constexpr int FN = 4;           // wave tile (BM/2) x 64
+  constexpr int FM = BM / 32;     // 16-row MFMA tiles per wave
+  constexpr int WROWS = BM / 2;   // rows per wave
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
-  const int64_t mt = (m + BIG_BM - 1) / BIG_BM, nt = (n + BIG_BN - 1) / BIG_BN;
+  const int64_t mt = (m + BM - 1) / BM, nt = (n + BIG_BN - 1) / BIG_BN;
   int64_t tile_m, tile_n;
   xcd_tile(blockIdx.x, mt * nt, nt, tile_m, tile_n);
-  const int64_t m0 = tile_m * BIG_BM, n0 = tile_n * BIG_BN;
+  const int64_t m0 = tile_m * BM, n0 = tile_n * BIG_BN;
   const int64_t KT = k / GBK;
   const int64_t NSS = KT >> 2;   // K is a multiple of 256
   const int64_t half_k = k >> 1, ngroups = k >> GSHIFT;
@@ -570,7 +577,7 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
 
   // ---- loaders: wave w fills rows 32w .. 32w+31 of each tile, eight rows
   // (8 lanes x 16 bytes) per instruction
-  const int64_t a_rows = min((int64_t)BIG_BM, m - m0);
+  const int64_t a_rows = min((int64_t)BM, m - m0);
   const int64_t b_rows = min((int64_t)BIG_BN, n - n0);
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(xh + m0 * k), (short)0, (int)(a_rows * k * 2), 0x00020000);
@@ -619,19 +626,20 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     for (int qq = 0; qq < 4; ++qq) bq_issue(ss, qq, bbuf, sbuf);
   };
 
-  // Fragment addresses: for rows r = (128 wm | 64 wn) + fr + 16 i the swizzle
-  // equals a_swz(fr), so row steps are immediate offsets.
+  // Fragment addresses: for rows r = (WROWS wm | 64 wn) + fr + 16 i the
+  // swizzle equals a_swz(fr) (WROWS and 16 are multiples of 16), so row
+  // steps are immediate offsets.
   const int swa = a_swz(fr);
   uint32_t a_lane[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) a_lane[ks] = (128 * wm + fr) * 128 + 16 * ((2 * g + ks) ^ swa);
+  for (int ks = 0; ks < 2; ++ks) a_lane[ks] = (WROWS * wm + fr) * 128 + 16 * ((2 * g + ks) ^ swa);
   const int b_row0 = 64 * wn + fr;
   // scales of row r live at r * 16
   const uint32_t s_lane = b_row0 * 16 + 2 * ((16 * g) >> GSHIFT);
 
-  auto read_a = [&](half8 (&af)[8], const uint8_t* abase, int ks) {
+  auto read_a = [&](half8 (&af)[FM], const uint8_t* abase, int ks) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < FM; ++i)
       af[i] = *reinterpret_cast<const half8*>(abase + a_lane[ks] + i * 2048);
   };
   // B words (both half-steps) and scales of stage s of a super-stage
@@ -646,16 +654,16 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     }
   };
 
-  f32x4 acc[8][FN];
+  f32x4 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  auto mfma_step = [&](const half8 (&af)[8], const half8 (&bj)[FN]) {
+  auto mfma_step = [&](const half8 (&af)[FM], const half8 (&bj)[FN]) {
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < FM; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bj[j], acc[i][j], 0, 0, 0);
   };
   auto sync = [&]() {
@@ -673,7 +681,7 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
   b_issue(0, big_b0, big_s0);
   bq_issue(min((int64_t)1, NSS - 1), 0, big_b1, big_s1);
   sync();
-  half8 af0[8], af1[8], bj0[FN], bj1[FN];
+  half8 af0[FM], af1[FM], bj0[FN], bj1[FN];
   uint32_t bw1[FN];
   _Float16 bsc[FN];
   {
@@ -702,7 +710,7 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
 #pragma unroll
     for (int j = 0; j < FN; ++j) bj1[j] = dequant8_f16(bw1[j], bsc[j]);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < FM; ++t) {
       SQ_GROUP(0x008, 1);
       SQ_GROUP(0x100, 1);
       SQ_GROUP(0x008, 1);
@@ -736,13 +744,13 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
       SQ_GROUP(0x020, 6);
       SQ_GROUP(0x100, 8);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < FM; ++t) {
         SQ_GROUP(0x008, 1);
         SQ_GROUP(0x100, 1);
         SQ_GROUP(0x008, 1);
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < FM; ++t) {
         SQ_GROUP(0x008, 1);
         SQ_GROUP(0x002, 4);
         SQ_GROUP(0x008, 1);
@@ -753,15 +761,15 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
   }
 #undef SQ_GROUP
 
-  const int64_t rbase = m0 + 128 * wm, cbase = n0 + 64 * wn;
+  const int64_t rbase = m0 + WROWS * wm, cbase = n0 + 64 * wn;
   // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA into the same accumulators
   for (int rr = 0; rr < rank; rr += 32) {
 #pragma unroll
     for (int hl = 0; hl < 2; ++hl) {
       const uint16_t* tsrc = hl ? tlo : thi;
-      bf16x8 af[8];
+      bf16x8 af[FM];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < FM; ++i) {
         const int64_t r = min(rbase + 16 * i + fr, m - 1);
         af[i] = *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + 8 * g);
       }
@@ -770,7 +778,7 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
         const int64_t c = min(cbase + 16 * j + fr, n - 1);
         const bf16x8 bj = *reinterpret_cast<const bf16x8*>(up + c * rank + rr + 8 * g);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < FM; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bj, acc[i][j], 0, 0, 0);
       }
     }
@@ -778,16 +786,16 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
 
   const int lr4 = 4 * g;
   if (y_bf16) {
-    // Each wave stages its 128 x 64 bf16 sub-tile (16 KB, 128-byte rows with
-    // the chunk swizzle) in half of a pipeline buffer, then stores eight whole
-    // 128-byte row segments per instruction.
+    // Each wave stages its WROWS x 64 bf16 sub-tile (at most 16 KB, 128-byte
+    // rows with the chunk swizzle) in half of a pipeline buffer, then stores
+    // eight whole 128-byte row segments per instruction.
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);   // the final (unused) prefetches have landed
     __syncthreads();                        // every wave is done with the pipeline buffers
     const int wb = wave >> 1;
     uint8_t* st = (wb == 0 ? big_a0 : wb == 1 ? big_a1 : wb == 2 ? big_b0 : big_b1) +
                   (wave & 1) * 16384;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int lrow = 16 * i + lr4 + v;
@@ -805,7 +813,7 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const bool full_cols = (cbase + 64 <= n) && ((n & 7) == 0);
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < WROWS / 8; ++it) {
       const int lrow = 8 * it + (lane >> 3), chunk = lane & 7;
       const int64_t r = rbase + lrow, c = cbase + 8 * chunk;
       const u32x4 o = *reinterpret_cast<const u32x4*>(st + lrow * 128 + 16 * (chunk ^ a_swz(lrow)));
@@ -821,7 +829,7 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t r = rbase + 16 * i + lr4 + v;
@@ -1009,13 +1017,25 @@ __global__ void __launch_bounds__(256) k_fwd_reduce(const float* __restrict__ pa
 // ---------------------------------------------------------------- host side
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Tile choice: the 256 x 256 tile when it yields at least half a tile per
-// CU, else 128 x 128 with split-K.
+// Tile choice: M <= 64 the small-M kernel; the big kernel when its grid has
+// at least half a tile per CU (with the tile height, 256 or 224, that needs
+// the fewest rows-times-rounds on the chip's 256 CUs); else 128 x 128 with
+// split-K.
 FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   FwdPlan p{};
   p.m = m; p.n = n; p.k = k; p.group = group; p.rank = rank;
   const int64_t KT = k / GBK;
-  const int64_t big_tiles = ((m + BIG_BM - 1) / BIG_BM) * ((n + BIG_BN - 1) / BIG_BN);
+  const int64_t nt_big = (n + BIG_BN - 1) / BIG_BN;
+  int big_bm = 256;
+  {
+    int64_t best = -1;
+    for (int bm : {256, 224}) {
+      const int64_t rounds = (((m + bm - 1) / bm) * nt_big + 255) / 256;
+      const int64_t cost = rounds * bm;
+      if (best < 0 || cost < best) { best = cost; big_bm = bm; }
+    }
+  }
+  const int64_t big_tiles = ((m + big_bm - 1) / big_bm) * nt_big;
   p.skinny_mt = 0;
   if (m <= 64) {
     // small M: 16-row tiles rounded up to 1, 2 or 4; split K into slices
@@ -1035,7 +1055,7 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
     p.splits = (int)((chunks + per - 1) / per);
     p.tile_m = 16 * p.skinny_mt; p.tile_n = SK_ROWS;
   } else if (big_tiles >= 128) {
-    p.tile_m = BIG_BM; p.tile_n = BIG_BN; p.splits = 1;
+    p.tile_m = big_bm; p.tile_n = BIG_BN; p.splits = 1;
   } else {
     p.tile_m = 128; p.tile_n = 128;
     const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
@@ -1128,14 +1148,16 @@ hipError_t launch_fwd_contract(const FwdPlan& p, const uint8_t* codes, const uin
     }
 #undef SQ_SKINNY
   } else if (p.tile_n == BIG_BN) {
-    if (p.group == 32)
-      hipLaunchKernelGGL(k_fwd_gemm_big<5>, dim3((unsigned)tiles), dim3(BIG_THREADS), 0, stream,
-                         b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k,
-                         p.rank, y_bf16);
-    else
-      hipLaunchKernelGGL(k_fwd_gemm_big<6>, dim3((unsigned)tiles), dim3(BIG_THREADS), 0, stream,
-                         b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k,
-                         p.rank, y_bf16);
+#define SQ_BIG(GS, BM)                                                                          \
+  hipLaunchKernelGGL((k_fwd_gemm_big<GS, BM>), dim3((unsigned)tiles), dim3(BIG_THREADS), 0,     \
+                     stream, b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k, \
+                     p.rank, y_bf16)
+    if (p.group == 32) {
+      if (p.tile_m == 224) SQ_BIG(5, 224); else SQ_BIG(5, 256);
+    } else {
+      if (p.tile_m == 224) SQ_BIG(6, 224); else SQ_BIG(6, 256);
+    }
+#undef SQ_BIG
   } else {
     hipLaunchKernelGGL(k_fwd_gemm<CfgMid>, grid, dim3(CfgMid::THREADS), CfgMid::LDS_BYTES, stream,
                        b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, b.partial, p.m, p.n,
