@@ -277,16 +277,24 @@ __device__ __forceinline__ void dequant32_f16(uint32_t (&out)[16], const u32x4& 
   }
 }
 
-// Map the linear workgroup id to a tile so that the workgroups resident on one
-// XCD at a time (ids congruent mod 8 are dispatched to the same XCD) walk
-// consecutive tiles in m-major order and share their activation rows in L2.
+// Map the linear workgroup id to a tile.  Ids congruent mod 8 are dispatched
+// to the same XCD, so each XCD gets one contiguous run of tile numbers; within
+// the run the numbers walk XCD_GROUP_M tile rows down before stepping one tile
+// column across, so the ~32 workgroups resident on an XCD at a time cover a
+// 4 x 8 block of tiles and share both operands in its L2 (4 A strips + 8 B
+// strips instead of 1 + 32).
+constexpr int64_t XCD_GROUP_M = 4;
 __device__ __forceinline__ void xcd_tile(int64_t lin, int64_t tiles, int64_t nt, int64_t& tm,
                                          int64_t& tn) {
   const int64_t xcd = lin & 7, idx = lin >> 3;
   const int64_t per = tiles >> 3, rem = tiles & 7;
   const int64_t t = xcd * per + min(xcd, rem) + idx;
-  tm = t / nt;
-  tn = t - tm * nt;
+  const int64_t mt = tiles / nt;
+  const int64_t grp = t / (XCD_GROUP_M * nt), first = grp * XCD_GROUP_M;
+  const int64_t gsz = min(XCD_GROUP_M, mt - first);
+  const int64_t w = t - grp * XCD_GROUP_M * nt;
+  tm = first + w % gsz;
+  tn = w / gsz;
 }
 
 template <class C>
