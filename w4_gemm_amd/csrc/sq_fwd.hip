@@ -904,7 +904,7 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       cw[t] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off + c_off[t] + (uint32_t)(kb >> 1), 0,
-                                                    SQ_CPOL_NT);
+                                                    0);
       sc[t] = __builtin_amdgcn_raw_buffer_load_b16(
           s_rsrc, off + s_off[t] + (uint32_t)(((kb + 32 * g) >> GSHIFT) * 2), 0, 0);
     }
