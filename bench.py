@@ -83,7 +83,7 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--ops", default="fwd,reconstruct,quantize,smallm")
+    ap.add_argument("--ops", default="fwd,reconstruct,quantize,smallm,configs")
     ap.add_argument("--small-m", default="1,16,128")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -185,6 +185,10 @@ def main():
             b.record()
         torch.cuda.synchronize()
         res["quantize"] = np.array([a.elapsed_time(b) for a, b in marks])
+    # ---------------------------------------------------------------- other shapes
+    if "configs" in ops:
+        res["configs"] = other_configs(torch, W, dev, [2, 3, 5], max(5, args.steps // 5),
+                                       args.warmup)
     # ---------------------------------------------------------------- small-M sweep
     if "smallm" in ops and args.small_m:
         res["smallm"] = small_m_sweep(torch, W, dev, [int(v) for v in args.small_m.split(",")],
@@ -232,6 +236,8 @@ def main():
         out["quantize_pct_hbm_peak"] = 100.0 * out["quantize_gbps"] / PEAK_HBM_GBPS
     if "smallm" in res:
         out["fwd_small_m"] = res["smallm"]
+    if "configs" in res:
+        out["fwd_other_configs"] = res["configs"]
 
     line = {
         "metric": "fused W4 fwd TFLOP/s (% bf16 MFMA peak) at 4480x16384x6144; reconstruct GB/s",
@@ -286,6 +292,52 @@ def copy_calibration(torch, dev, reps=5):
     return 0
 
 
+def layer(torch, W, dev, cfg_id):
+    """Synthetic layer of a configuration: its payload (quantized on the GPU
+    with randomized rank-R factors) and its activation draw (numpy bf16)."""
+    from synth import CONFIGS, gen_activations, gen_weight
+    cfg = CONFIGS[cfg_id]
+    rng = np.random.default_rng(0)
+    w = torch.from_numpy(gen_weight(rng, cfg.N, cfg.K, cfg.spike)).to(dev)
+    x_all = gen_activations(rng, cfg.M, cfg.K, cfg.outlier_frac)
+    torch.manual_seed(0)
+    u, s, v = torch.svd_lowrank(w, q=cfg.rank + 8, niter=2)
+    rs = s[:cfg.rank].sqrt()
+    up = (u[:, :cfg.rank] * rs).to(torch.bfloat16).contiguous()
+    down = (v[:, :cfg.rank] * rs).to(torch.bfloat16).contiguous()
+    p, _, flags = W.quantize_weight(w, up, down, cfg.group)
+    torch.cuda.synchronize()
+    assert int(flags[0]) == 0
+    return cfg, p, x_all
+
+
+def other_configs(torch, W, dev, ids, steps, warmup):
+    """The whole forward at the other layer shapes (their own M), timed per
+    call with HIP events on the current stream."""
+    out = {}
+    for cid in ids:
+        cfg, p, x_all = layer(torch, W, dev, cid)
+        M, N, K, R = cfg.M, cfg.N, cfg.K, cfg.rank
+        x = torch.from_numpy(x_all.view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(W.fwd_workspace_bytes(M, p), dtype=torch.uint8, device=dev)
+        for _ in range(warmup):
+            W.linear_fwd(x, p, out=y, workspace=ws)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            W.linear_fwd(x, p, out=y, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        fl = 2.0 * M * N * K + 2.0 * M * R * (N + K)
+        out[cfg.name] = {"us": t * 1e3, "tflops": fl / (t * 1e-3) / 1e12,
+                         "pct_mfma_peak": 100.0 * fl / (t * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
+        del p, x, y, ws
+    return out
+
+
 def small_m_sweep(torch, W, dev, ms, steps, warmup):
     """Forward at small M on the 6144x16384 g32 rank-32 weight, HBM-bound:
     GB/s of the bytes one call must move (payload + x + y), first M rows of
@@ -293,21 +345,8 @@ def small_m_sweep(torch, W, dev, ms, steps, warmup):
     less time than the host needs to enqueue them, so the calls are captured
     once in a HIP graph and the graph is replayed: the figure is GPU time
     per call (`us`), with the eager per-call time beside it (`eager_us`)."""
-    from synth import CONFIGS, gen_activations, gen_weight
-    cfg = CONFIGS[5]
+    cfg, p, x_all = layer(torch, W, dev, 5)
     N, K, G, R = cfg.N, cfg.K, cfg.group, cfg.rank
-    rng = np.random.default_rng(0)
-    w = torch.from_numpy(gen_weight(rng, N, K, cfg.spike)).to(dev)
-    x_all = gen_activations(rng, cfg.M, K, cfg.outlier_frac)
-    torch.manual_seed(0)
-    u, s, v = torch.svd_lowrank(w, q=R + 8, niter=2)
-    rs = s[:R].sqrt()
-    up = (u[:, :R] * rs).to(torch.bfloat16).contiguous()
-    down = (v[:, :R] * rs).to(torch.bfloat16).contiguous()
-    p, _, flags = W.quantize_weight(w, up, down, G)
-    torch.cuda.synchronize()
-    assert int(flags[0]) == 0
-    del w, u, v
     pay = N * K / 2 + N * (K // G) * 2 + (N + K) * R * 2
     out = {}
     for m in ms:

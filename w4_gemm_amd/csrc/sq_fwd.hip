@@ -171,20 +171,25 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
   }
   __syncthreads();
 
-  if (blockIdx.y == 0) {
-    // t slices in a fixed order, scaled, split into bf16 hi + lo
-    for (int i = tid; i < 16 * rank; i += 64 * PRE_WAVES) {
+  {
+    // t slices in a fixed order, scaled, split into bf16 hi + lo; the 16 x
+    // rank outputs of the strip are shared out over its column groups, and
+    // each output's slice loads go out eight at a time
+    const int outs = 16 * rank;
+    const int per = (outs + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int i0 = (int)blockIdx.y * per, i1 = min(outs, i0 + per);
+    for (int i = i0 + tid; i < i1; i += 64 * PRE_WAVES) {
       const int rr = i / rank, r = i - rr * rank;
       const int64_t row = row0 + rr;
       if (row >= m) continue;
       float t = 0.0f;
       int q = 0;
-      for (; q + 4 <= slices; q += 4) {
-        float v[4];
+      for (; q + 8 <= slices; q += 8) {
+        float v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = t_part[((q + u) * m + row) * rank + r];
+        for (int u = 0; u < 8; ++u) v[u] = t_part[((q + u) * m + row) * rank + r];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) t += v[u];
+        for (int u = 0; u < 8; ++u) t += v[u];
       }
       for (; q < slices; ++q) t += t_part[(q * m + row) * rank + r];
       t *= ldexpf(1.0f, 11 - s_exp[rr]);
@@ -192,7 +197,8 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
       thi[row * rank + r] = hb;
       tlo[row * rank + r] = f32_to_bf16(t - bf16_to_f32(hb));
     }
-    if (tid < 16 && row0 + tid < m) rowscale[row0 + tid] = ldexpf(1.0f, s_exp[tid] - 11);
+    if (blockIdx.y == 0 && tid < 16 && row0 + tid < m)
+      rowscale[row0 + tid] = ldexpf(1.0f, s_exp[tid] - 11);
   }
   const int64_t b = (int64_t)blockIdx.y * PRE_WAVES + wave;
   if (b >= nblk) return;
@@ -239,43 +245,9 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
   }
 }
 
-// ---------------------------------------------------------------- main contraction
-// Tile configuration: BM x BN output tile per workgroup, WAVES_M x WAVES_N
-// waves, each owning a (BM/WAVES_M) x (BN/WAVES_N) sub-tile of 16x16 MFMA
-// tiles; K advances 64 per stage (two 16x16x32 MFMA steps), double-buffered
-// in LDS.
-constexpr int GBK = 64, LDS_STRIDE = GBK + 8;   // halves per LDS row (16-byte pad)
-
-template <int BM_, int BN_, int WM_, int WN_>
-struct GemmCfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WM_, WAVES_N = WN_;
-  static constexpr int THREADS = 64 * WM_ * WN_;
-  static constexpr int FM = BM_ / WM_ / 16, FN = BN_ / WN_ / 16;
-  static constexpr int A_PIECES = BM_ * 8 / THREADS;   // 16-byte pieces of A per thread
-  static constexpr int B_PIECES = BN_ * 2 / THREADS;   // 32-code pieces of B per thread
-  static constexpr size_t LDS_BYTES = (size_t)2 * (BM_ + BN_) * LDS_STRIDE * 2;
-  static_assert(A_PIECES * THREADS == BM_ * 8 && B_PIECES * THREADS == BN_ * 2, "tile/threads");
-};
-
-using CfgMid = GemmCfg<128, 128, 2, 2>;
-
-// 32 packed codes (one 16-byte load) -> 16 fp16 pairs of q*s, in the permuted
-// K order: pair p of word j holds codes (8j+p, 8j+p+4).
-__device__ __forceinline__ void dequant32_f16(uint32_t (&out)[16], const u32x4& w, _Float16 s) {
-  const half2v sv = {s, s};
-  const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t word = w[j] ^ 0x88888888u;   // nibble ^ 8 = q + 8
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t bits = ((word >> (4 * p)) & 0x000F000Fu) | 0x64006400u;   // 1024 + q + 8
-      half2v h = __builtin_bit_cast(half2v, bits);
-      h = (h - off) * sv;
-      out[4 * j + p] = __builtin_bit_cast(uint32_t, h);
-    }
-  }
-}
+// ---------------------------------------------------------------- contraction
+// K advances 64 values per pipeline stage (two 16x16x32 MFMA steps).
+constexpr int GBK = 64;
 
 // Map the linear workgroup id to a tile.  Ids congruent mod 8 are dispatched
 // to the same XCD, so each XCD gets one contiguous run of tile numbers; within
@@ -297,203 +269,9 @@ __device__ __forceinline__ void xcd_tile(int64_t lin, int64_t tiles, int64_t nt,
   tn = w / gsz;
 }
 
-template <class C>
-__global__ void __launch_bounds__(C::THREADS) k_fwd_gemm(
-    const uint16_t* __restrict__ xh, const uint8_t* __restrict__ codes,
-    const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
-    const uint16_t* __restrict__ tlo, const uint16_t* __restrict__ up,
-    const float* __restrict__ rowscale, void* __restrict__ y, float* __restrict__ partial,
-    int64_t m, int64_t n, int64_t k, int group, int rank, int splits, int y_bf16) {
-  extern __shared__ __attribute__((aligned(16))) _Float16 lds[];
-  _Float16 (*As)[C::BM][LDS_STRIDE] = reinterpret_cast<_Float16 (*)[C::BM][LDS_STRIDE]>(lds);
-  _Float16 (*Bs)[C::BN][LDS_STRIDE] =
-      reinterpret_cast<_Float16 (*)[C::BN][LDS_STRIDE]>(lds + 2 * C::BM * LDS_STRIDE);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
-  const int64_t mt = (m + C::BM - 1) / C::BM, nt = (n + C::BN - 1) / C::BN;
-  int64_t tile_m, tile_n;
-  xcd_tile(blockIdx.x, mt * nt, nt, tile_m, tile_n);
-  const int64_t m0 = tile_m * C::BM, n0 = tile_n * C::BN;
-  const int z = blockIdx.y;
-  const int64_t KT = k / GBK;
-  const int64_t per = (KT + splits - 1) / splits;
-  const int64_t kt0 = min((int64_t)z * per, KT), kt1 = min(kt0 + per, KT);
-  const int64_t ngroups = k / group;
-  const int64_t half_k = k >> 1;
-
-  u32x4 a_reg[C::A_PIECES];
-  u32x4 b_reg[C::B_PIECES];
-  _Float16 s_reg[C::B_PIECES];
-  auto gload = [&](int64_t kt) {
-#pragma unroll
-    for (int p = 0; p < C::A_PIECES; ++p) {
-      const int gp = tid + C::THREADS * p;
-      const int64_t r = m0 + (gp >> 3);
-      a_reg[p] = r < m ? *reinterpret_cast<const u32x4*>(xh + r * k + kt * GBK + 8 * (gp & 7))
-                       : (u32x4){0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int p = 0; p < C::B_PIECES; ++p) {
-      const int gp = tid + C::THREADS * p;
-      const int64_t r = n0 + (gp >> 1);
-      const int64_t kk = kt * GBK + 32 * (gp & 1);
-      if (r < n) {
-        b_reg[p] = *reinterpret_cast<const u32x4*>(codes + r * half_k + (kk >> 1));
-        s_reg[p] = __builtin_bit_cast(_Float16, scales[r * ngroups + kk / group]);
-      } else {
-        b_reg[p] = (u32x4){0, 0, 0, 0};
-        s_reg[p] = (_Float16)0.0f;
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < C::A_PIECES; ++p) {
-      const int gp = tid + C::THREADS * p;
-      *reinterpret_cast<u32x4*>(&As[buf][gp >> 3][8 * (gp & 7)]) = a_reg[p];
-    }
-#pragma unroll
-    for (int p = 0; p < C::B_PIECES; ++p) {
-      const int gp = tid + C::THREADS * p;
-      uint32_t bq[16];
-      dequant32_f16(bq, b_reg[p], s_reg[p]);
-      u32x4* bd = reinterpret_cast<u32x4*>(&Bs[buf][gp >> 1][32 * (gp & 1)]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bd[j] = (u32x4){bq[4 * j], bq[4 * j + 1], bq[4 * j + 2], bq[4 * j + 3]};
-    }
-  };
-
-  f32x4 acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-  const int fr = lane & 15, fk = 8 * (lane >> 4);
-  if (kt0 < kt1) {
-    gload(kt0);
-    lstore(0);
-    __syncthreads();
-    for (int64_t kt = kt0; kt < kt1; ++kt) {
-      const int buf = (int)((kt - kt0) & 1);
-      const bool more = kt + 1 < kt1;
-      if (more) gload(kt + 1);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        half8 af[C::FM];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-          af[i] = *reinterpret_cast<const half8*>(
-              &As[buf][wm * (C::BM / C::WAVES_M) + 16 * i + fr][32 * ks + fk]);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const half8 bj = *reinterpret_cast<const half8*>(
-              &Bs[buf][wn * (C::BN / C::WAVES_N) + 16 * j + fr][32 * ks + fk]);
-#pragma unroll
-          for (int i = 0; i < C::FM; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bj, acc[i][j], 0, 0, 0);
-        }
-      }
-      if (more) lstore(buf ^ 1);
-      __syncthreads();
-    }
-  }
-
-  const int64_t rbase = m0 + wm * (C::BM / C::WAVES_M);
-  const int64_t cbase = n0 + wn * (C::BN / C::WAVES_N);
-  // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA, added once (split 0)
-  if (z == 0) {
-    for (int rr = 0; rr < rank; rr += 32) {
-#pragma unroll
-      for (int hl = 0; hl < 2; ++hl) {
-        const uint16_t* tsrc = hl ? tlo : thi;
-        bf16x8 af[C::FM], bfr[C::FN];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i) {
-          const int64_t r = rbase + 16 * i + fr;
-          af[i] = r < m ? *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + fk) : (bf16x8){};
-        }
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) {
-          const int64_t cc = cbase + 16 * j + fr;
-          bfr[j] = cc < n ? *reinterpret_cast<const bf16x8*>(up + cc * rank + rr + fk) : (bf16x8){};
-        }
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-
-  // epilogue: lane holds rows 4*(lane/16)+v of each 16x16 tile, column lane%16
-  const int lr4 = 4 * (lane >> 4);
-  if (splits == 1 && y_bf16) {
-    // stage the bf16 tile in LDS (the operand buffers are free: the loop ended
-    // with a barrier) and store whole row segments
-    constexpr int SROW = C::BN + 8;   // halves per staged row
-    uint16_t* st = reinterpret_cast<uint16_t*>(lds);
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int lrow = wm * (C::BM / C::WAVES_M) + 16 * i + lr4 + v;
-        const int64_t r = m0 + lrow;
-        const float rs = r < m ? rowscale[r] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j)
-          st[lrow * SROW + wn * (C::BN / C::WAVES_N) + 16 * j + fr] = f32_to_bf16(acc[i][j][v] * rs);
-      }
-    }
-    __syncthreads();
-    constexpr int PIECES = C::BM * C::BN / 8;   // 16-byte pieces of the tile
-    constexpr int PER_ROW = C::BN / 8;
-#pragma unroll 4
-    for (int gp = tid; gp < PIECES; gp += C::THREADS) {
-      const int lrow = gp / PER_ROW, piece = gp % PER_ROW;
-      const int64_t r = m0 + lrow, cc = n0 + 8 * piece;
-      if (r >= m) continue;
-      const u32x4 o = *reinterpret_cast<const u32x4*>(&st[lrow * SROW + 8 * piece]);
-      uint16_t* dst = reinterpret_cast<uint16_t*>(y) + r * n + cc;
-      if (cc + 8 <= n && ((n & 7) == 0)) {
-        *reinterpret_cast<u32x4*>(dst) = o;
-      } else {
-        const uint16_t* h = reinterpret_cast<const uint16_t*>(&o);
-        for (int e = 0; e < 8 && cc + e < n; ++e) dst[e] = h[e];
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t r = rbase + 16 * i + lr4 + v;
-      if (r >= m) continue;
-      const float rs = rowscale[r];
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int64_t cc = cbase + 16 * j + fr;
-        if (cc >= n) continue;
-        if (splits > 1) {
-          partial[((int64_t)z * m + r) * n + cc] = acc[i][j][v];
-        } else if (y_bf16) {
-          reinterpret_cast<uint16_t*>(y)[r * n + cc] = f32_to_bf16(acc[i][j][v] * rs);
-        } else {
-          reinterpret_cast<float*>(y)[r * n + cc] = acc[i][j][v] * rs;
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- large-tile contraction
-// 256 x 256 output tile per workgroup, eight waves of 128 x 64 (8 x 4 MFMA
-// tiles each, two waves per SIMD).
+// BM x 256 output tile per workgroup (BM = 256, 224 or 128), eight waves of
+// (BM/2) x 64 ((BM/32) x 4 MFMA tiles each, two waves per SIMD).
 //
 // Data path: everything streams global -> LDS with direct 16-byte buffer
 // loads (no register staging) into tiles of 128-byte rows whose 16-byte chunk
@@ -555,18 +333,22 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0], expcnt [6:4], lgkmcnt [11:8])
 constexpr int WAIT_VM0 = 0x0F70, WAIT_LGKM0 = 0xC07F;
 
-// BM: tile rows, 256 or 224 (the LDS A tile always has 256 rows; with 224 the
-// last 32 load a clamped row and are not read).  plan_fwd picks the height
-// that needs the fewest tile-rounds of the chip, so that M = 4480 fills five
-// whole rounds of 224-row tiles instead of 4.5 rounds of 256-row tiles.
-template <int GSHIFT, int BM>   // log2 of the group size, tile rows
+// BM: tile rows, 256, 224 or 128 (the LDS A tile always has 256 rows; loader
+// rows past BM fetch nothing).  Split-K: workgroup
+// (tile, z) covers stages [z kts, (z+1) kts) (kts a multiple of 4, so every
+// split starts on a super-stage) by shifting the three buffer bases; with
+// more than one split the fp32 partial sums, without the row scale, go to
+// `partial` [splits][m][n] for k_fwd_reduce, and split 0 adds the rank-r
+// branch.  plan_fwd picks BM and the split count.  SPLIT = false compiles
+// the single-split kernel without any of the split bookkeeping.
+template <int GSHIFT, int BM, bool SPLIT>   // log2 of the group size, tile rows, split-K
 __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     const uint16_t* __restrict__ xh, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
     const uint16_t* __restrict__ tlo, const uint16_t* __restrict__ up,
-    const float* __restrict__ rowscale, void* __restrict__ y, int64_t m, int64_t n, int64_t k,
-    int rank, int y_bf16) {
-  static_assert(BM == 256 || BM == 224, "tile rows");
+    const float* __restrict__ rowscale, void* __restrict__ y, float* __restrict__ partial,
+    int64_t m, int64_t n, int64_t k, int rank, int y_bf16, int kts) {
+  static_assert(BM == 256 || BM == 224 || BM == 128, "tile rows");
   constexpr int FN = 4;           // wave tile (BM/2) x 64
   constexpr int FM = BM / 32;     // 16-row MFMA tiles per wave
   constexpr int WROWS = BM / 2;   // rows per wave
@@ -578,26 +360,37 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
   int64_t tile_m, tile_n;
   xcd_tile(blockIdx.x, mt * nt, nt, tile_m, tile_n);
   const int64_t m0 = tile_m * BM, n0 = tile_n * BIG_BN;
-  const int64_t KT = k / GBK;
-  const int64_t NSS = KT >> 2;   // K is a multiple of 256
+  const int z = SPLIT ? (int)blockIdx.y : 0;
+  const int64_t kt0 = SPLIT ? (int64_t)z * kts : 0;   // first stage of this split
+  const int64_t KT = SPLIT ? (int64_t)kts : k / GBK;
+  const int64_t NSS = KT >> 2;            // kts is a multiple of 4
   const int64_t half_k = k >> 1, ngroups = k >> GSHIFT;
+
   const int fr = lane & 15, g = lane >> 4;
 
   // ---- loaders: wave w fills rows 32w .. 32w+31 of each tile, eight rows
   // (8 lanes x 16 bytes) per instruction
   const int64_t a_rows = min((int64_t)BM, m - m0);
   const int64_t b_rows = min((int64_t)BIG_BN, n - n0);
+  // bases at this split's first K value (64 kt0 values: 128 bytes of xh,
+  // 32 bytes of codes, 64 kt0 / group scales per row)
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(xh + m0 * k), (short)0, (int)(a_rows * k * 2), 0x00020000);
+      (void*)(xh + m0 * k + kt0 * GBK), (short)0, (int)(a_rows * k * 2 - kt0 * GBK * 2),
+      0x00020000);
   const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(codes + n0 * half_k), (short)0, (int)(b_rows * half_k), 0x00020000);
+      (void*)(codes + n0 * half_k + kt0 * (GBK / 2)), (short)0,
+      (int)(b_rows * half_k - kt0 * (GBK / 2)), 0x00020000);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(scales + n0 * ngroups), (short)0, (int)(b_rows * ngroups * 2), 0x00020000);
+      (void*)(scales + n0 * ngroups + ((kt0 * GBK) >> GSHIFT)), (short)0,
+      (int)(b_rows * ngroups * 2 - ((kt0 * GBK) >> GSHIFT) * 2), 0x00020000);
   uint32_t a_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 32 * wave + 8 * i + (lane >> 3);
-    a_off[i] = (uint32_t)(min((int64_t)r, a_rows - 1) * k * 2) + 16 * ((lane & 7) ^ a_swz(r));
+    // loader rows at or past BM are never read: an offset past the
+    // descriptor's range makes their loads fetch nothing (no branch)
+    a_off[i] = r < BM ? (uint32_t)(min((int64_t)r, a_rows - 1) * k * 2) + 16 * ((lane & 7) ^ a_swz(r))
+                      : 0x80000000u;
   }
 
   auto a_issue = [&](int64_t kt, uint8_t* buf) {
@@ -771,7 +564,7 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
 
   const int64_t rbase = m0 + WROWS * wm, cbase = n0 + 64 * wn;
   // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA into the same accumulators
-  for (int rr = 0; rr < rank; rr += 32) {
+  for (int rr = 0; rr < (z == 0 ? rank : 0); rr += 32) {   // (z is 0 unless SPLIT)
 #pragma unroll
     for (int hl = 0; hl < 2; ++hl) {
       const uint16_t* tsrc = hl ? tlo : thi;
@@ -793,6 +586,24 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
   }
 
   const int lr4 = 4 * g;
+  if constexpr (SPLIT) {
+    // split-K partial sums (no row scale): k_fwd_reduce finishes them
+    float* pz = partial + (int64_t)z * m * n;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t r = rbase + 16 * i + lr4 + v;
+        if (r >= m) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t c = cbase + 16 * j + fr;
+          if (c < n) pz[r * n + c] = acc[i][j][v];
+        }
+      }
+    }
+    return;
+  }
   if (y_bf16) {
     // Each wave stages its WROWS x 64 bf16 sub-tile (at most 16 KB, 128-byte
     // rows with the chunk swizzle) in half of a pipeline buffer, then stores
@@ -1033,17 +844,6 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   FwdPlan p{};
   p.m = m; p.n = n; p.k = k; p.group = group; p.rank = rank;
   const int64_t KT = k / GBK;
-  const int64_t nt_big = (n + BIG_BN - 1) / BIG_BN;
-  int big_bm = 256;
-  {
-    int64_t best = -1;
-    for (int bm : {256, 224}) {
-      const int64_t rounds = (((m + bm - 1) / bm) * nt_big + 255) / 256;
-      const int64_t cost = rounds * bm;
-      if (best < 0 || cost < best) { best = cost; big_bm = bm; }
-    }
-  }
-  const int64_t big_tiles = ((m + big_bm - 1) / big_bm) * nt_big;
   p.skinny_mt = 0;
   if (m <= 64) {
     // small M: 16-row tiles rounded up to 1, 2 or 4; split K into slices
@@ -1062,14 +862,25 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
     p.skinny_kslice = (int)(per * 256);
     p.splits = (int)((chunks + per - 1) / per);
     p.tile_m = 16 * p.skinny_mt; p.tile_n = SK_ROWS;
-  } else if (big_tiles >= 128) {
-    p.tile_m = big_bm; p.tile_n = BIG_BN; p.splits = 1;
   } else {
-    p.tile_m = 128; p.tile_n = 128;
-    const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
-    int64_t s = (512 + tiles - 1) / tiles;
-    s = std::min<int64_t>(s, std::max<int64_t>(1, KT / 8));
-    p.splits = (int)std::max<int64_t>(s, 1);
+    // The 256-column-tile kernel with tile height BM in {256, 224, 128} and
+    // s K splits (whole super-stages each).  Estimated time: tile-rounds of
+    // the 256 CUs times BM x stages per split (about 7.8 ns per row-stage
+    // per resident tile, measured), plus writing and re-reading the fp32
+    // partials at ~5 TB/s when s > 1.
+    const int64_t nt_big = (n + BIG_BN - 1) / BIG_BN;
+    double best = -1.0;
+    for (int bm : {256, 224, 128}) {
+      const int64_t tiles = ((m + bm - 1) / bm) * nt_big;
+      for (int64_t sp = 1; sp <= 16; sp *= 2) {
+        if ((KT / 4) % sp) continue;   // every split a whole number of super-stages
+        const int64_t rounds = (tiles * sp + 255) / 256;
+        double t = rounds * (double)bm * (double)(KT / sp) * 7.8e-9;
+        if (sp > 1) t += 8.0 * sp * (double)m * n / 5e12 + 3e-6;
+        if (best < 0.0 || t < best - 1e-9) { best = t; p.tile_m = bm; p.splits = (int)sp; }
+      }
+    }
+    p.tile_n = BIG_BN;
   }
   size_t off = 0;
   p.off_xh = off;        off = align256(off + (size_t)m * k * 2);
@@ -1155,21 +966,22 @@ hipError_t launch_fwd_contract(const FwdPlan& p, const uint8_t* codes, const uin
       if (p.skinny_mt == 1) SQ_SKINNY(6, 1); else if (p.skinny_mt == 2) SQ_SKINNY(6, 2); else SQ_SKINNY(6, 4);
     }
 #undef SQ_SKINNY
-  } else if (p.tile_n == BIG_BN) {
-#define SQ_BIG(GS, BM)                                                                          \
-  hipLaunchKernelGGL((k_fwd_gemm_big<GS, BM>), dim3((unsigned)tiles), dim3(BIG_THREADS), 0,     \
-                     stream, b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, p.m, p.n, p.k, \
-                     p.rank, y_bf16)
-    if (p.group == 32) {
-      if (p.tile_m == 224) SQ_BIG(5, 224); else SQ_BIG(5, 256);
-    } else {
-      if (p.tile_m == 224) SQ_BIG(6, 224); else SQ_BIG(6, 256);
-    }
-#undef SQ_BIG
   } else {
-    hipLaunchKernelGGL(k_fwd_gemm<CfgMid>, grid, dim3(CfgMid::THREADS), CfgMid::LDS_BYTES, stream,
-                       b.xh, codes, scales, b.thi, b.tlo, up, b.rowscale, y, b.partial, p.m, p.n,
-                       p.k, p.group, p.rank, p.splits, y_bf16);
+    const int kts = (int)(p.k / GBK / p.splits);
+#define SQ_BIG(GS, BM, SP)                                                                      \
+  hipLaunchKernelGGL((k_fwd_gemm_big<GS, BM, SP>), grid, dim3(BIG_THREADS), 0, stream, b.xh,    \
+                     codes, scales, b.thi, b.tlo, up, b.rowscale, y, b.partial, p.m, p.n, p.k,   \
+                     p.rank, y_bf16, kts)
+#define SQ_BIG_BM(GS, SP)                                                                       \
+  if (p.tile_m == 224) SQ_BIG(GS, 224, SP); else if (p.tile_m == 256) SQ_BIG(GS, 256, SP);     \
+  else SQ_BIG(GS, 128, SP)
+    if (p.group == 32) {
+      if (p.splits > 1) { SQ_BIG_BM(5, true); } else { SQ_BIG_BM(5, false); }
+    } else {
+      if (p.splits > 1) { SQ_BIG_BM(6, true); } else { SQ_BIG_BM(6, false); }
+    }
+#undef SQ_BIG_BM
+#undef SQ_BIG
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (p.splits > 1 || p.skinny_mt > 0) {
