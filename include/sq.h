@@ -40,11 +40,12 @@ extern "C" {
 typedef enum {
   SQ_OK = 0,
   SQ_E_NULL = 1,      /* a required pointer is NULL                               */
-  SQ_E_SHAPE = 2,     /* K % 256 != 0, K < 256, N < 1 or M < 0                    */
+  SQ_E_SHAPE = 2,     /* K % 256 != 0, K < 256, N < 1 or M < 0; the input         */
+                      /* gradient also needs N % 64 == 0                          */
   SQ_E_GROUP = 3,     /* group is not 32 or 64                                    */
   SQ_E_RANK = 4,      /* rank is not 0, 32 or 64                                  */
   SQ_E_ALIGN = 5,     /* a pointer is not 16-byte aligned                         */
-  SQ_E_WORKSPACE = 6, /* workspace smaller than sq_linear_fwd_workspace_bytes()   */
+  SQ_E_WORKSPACE = 6, /* workspace smaller than the matching *_workspace_bytes()  */
   SQ_E_DTYPE = 7,     /* output dtype is not SQ_F32 or SQ_BF16                    */
   SQ_E_ARCH = 8,      /* the current device is not gfx950                         */
   SQ_E_HIP = 9        /* a HIP runtime call or kernel launch failed               */
@@ -123,6 +124,26 @@ sq_status_t sq_linear_fwd_contract(int64_t m, const sq_w4_t *p, void *y, sq_dtyp
  *   w_hat[n][k] = bf16_round_nearest_even( lora_up @ lora_down^T + dequant(R) @ H )
  * with every intermediate in fp32 and one rounding at the end. */
 sq_status_t sq_reconstruct_bf16(const sq_w4_t *p, uint16_t *w_hat, void *stream);
+
+/* Input gradient (the format formula transposed: dx = dy @ W_hat; where the
+ * page's backward first rebuilds the dense bf16 weight, this contracts the
+ * packed codes directly, and H H = I moves the rotation to the end):
+ *   dx = (dy @ dequant(R)) @ H + (dy @ lora_up) @ lora_down^T, that is
+ *   dx[m][k] = sum_j ( sum_n dy[m][n] q[n][j] s[n][j/group] ) H[j][k]
+ *            + sum_r (dy @ lora_up)[m][r] lora_down[k][r].
+ * dy is bf16 [m][n]; dx is fp32 or bf16 [m][k] (bf16 = round-to-nearest-even
+ * of the fp32 result).  N must be a multiple of 64.  The int4 contraction runs
+ * on fp16 MFMA with the same operand treatment as the forward: each row of dy
+ * is scaled by a power of two and rounded to fp16, the weight operand is
+ * fp16(q * s), accumulation is fp32; the rank-r term is carried as bf16 hi +
+ * lo parts.  `workspace` is device scratch of at least
+ * sq_linear_dgrad_workspace_bytes(m, p) bytes (0 for unsupported shapes),
+ * owned by the caller and not read before it is written.  m == 0 is a no-op
+ * that returns SQ_OK. */
+size_t sq_linear_dgrad_workspace_bytes(int64_t m, const sq_w4_t *p);
+sq_status_t sq_linear_dgrad(const uint16_t *dy, int64_t m, const sq_w4_t *p, void *dx,
+                            sq_dtype_t dx_dtype, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *sq_status_str(sq_status_t status);

@@ -318,6 +318,38 @@ def forward_fp16_operands(x, q, scale, up, down, group: int) -> np.ndarray:
     return y + (x @ np.asarray(down, np.float64)) @ np.asarray(up, np.float64).T
 
 
+def dgrad(dy, q, scale, up, down, group: int) -> np.ndarray:
+    """Input gradient of the layer: dx = dy @ W_hat in fp64.
+
+    From the format formula, dy @ (up @ down^T + D H) = (dy @ D) H +
+    (dy @ up) @ down^T with D = dequant(R): the int4 product contracts over
+    the output features and the rotation acts on its result's K blocks.
+    """
+    dy = np.asarray(dy, np.float64)
+    d = dequant(q, scale, group)
+    return rotate(dy @ d) + (dy @ np.asarray(up, np.float64)) @ np.asarray(down, np.float64).T
+
+
+def dgrad_fp16_operands(dy, q, scale, up, down, group: int) -> np.ndarray:
+    """Diagnostic input gradient: the int4 contraction's operands in fp16.
+
+    Each row of dy is multiplied by 2^(11-E), E = ceil(log2(max|dy_row|)),
+    and rounded to fp16; the dequantized weight is fp16(q*s); the product is
+    rotated, the row factor undone, and the low-rank term is exact.
+    """
+    dy = np.asarray(dy, np.float64)
+    amax = np.abs(dy).max(axis=1)
+    e = np.zeros(dy.shape[0])
+    nz = amax > 0
+    mant, ex = np.frexp(amax[nz])
+    e[nz] = np.where(mant == 0.5, ex - 1, ex)
+    f = np.ldexp(1.0, (11 - e).astype(np.int64))
+    dy16 = fp16_round(dy * f[:, None])
+    d16 = fp16_round(dequant(q, scale, group))
+    dx = rotate(dy16 @ d16) / f[:, None]
+    return dx + (dy @ np.asarray(up, np.float64)) @ np.asarray(down, np.float64).T
+
+
 # --------------------------------------------------------------------------
 # metrics
 # --------------------------------------------------------------------------

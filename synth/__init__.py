@@ -42,7 +42,7 @@ CONFIGS = {
     3: LayerConfig("fused-qkv 1536x9216x3072 g64", 1536, 9216, 3072, 64, 32, 8, 0.005),
     4: LayerConfig("mlp-up 4480x16384x6144 g32", 4480, 16384, 6144, 32, 32, 8, 0.005),
     5: LayerConfig("mlp-down 4480x6144x16384 g32", 4480, 6144, 16384, 32, 32, 8, 0.005,
-                   small_m=(1, 16, 128)),
+                   small_m=(1, 16, 32, 64, 128)),
 }
 
 

@@ -59,6 +59,7 @@ def test_validation_before_launch(why, kw, status):
     assert _lib.sq_reconstruct_bf16(p, 0x5000, None) == status
     assert _lib.sq_quantize_weight(0x6000, p, None, 0x7000, None) == status
     assert _lib.sq_linear_fwd(0x8000, 4, p, 0x9000, 0, 0xA000, 1 << 30, None) == status
+    assert _lib.sq_linear_dgrad(0x8000, 4, p, 0x9000, 0, 0xA000, 1 << 30, None) == status
 
 
 def test_other_arguments():
@@ -75,6 +76,24 @@ def test_other_arguments():
     # rank 0 needs no factors
     p0 = _payload(rank=0, up=None, down=None)
     assert _lib.sq_linear_fwd_workspace_bytes(4, p0) > 0
+
+
+def test_dgrad_arguments():
+    p = _payload(n=128)
+    big = 1 << 40
+    assert _lib.sq_linear_dgrad(0x8000, 4, _payload(n=16), 0x9000, 0, 0xA000, big, None) == 2
+    assert _lib.sq_linear_dgrad_workspace_bytes(4, _payload(n=16)) == 0
+    assert _lib.sq_linear_dgrad(0x8000, -1, p, 0x9000, 0, 0xA000, big, None) == 2
+    assert _lib.sq_linear_dgrad(0x8000, 4, p, 0x9000, 7, 0xA000, big, None) == 7
+    assert _lib.sq_linear_dgrad(0x8000, 0, p, 0x9000, 0, None, 0, None) == 0   # m == 0: no-op
+    assert _lib.sq_linear_dgrad(None, 4, p, 0x9000, 0, 0xA000, big, None) == 1
+    assert _lib.sq_linear_dgrad(0x8000, 4, p, None, 0, 0xA000, big, None) == 1
+    assert _lib.sq_linear_dgrad(0x8008, 4, p, 0x9000, 0, 0xA000, big, None) == 5
+    ws = _lib.sq_linear_dgrad_workspace_bytes(4, p)
+    assert ws >= 4 * 256 * 4                          # holds the fp32 accumulator
+    assert _lib.sq_linear_dgrad(0x8000, 4, p, 0x9000, 0, 0xA000, ws - 1, None) == 6
+    p0 = _payload(n=128, rank=0, up=None, down=None)
+    assert 0 < _lib.sq_linear_dgrad_workspace_bytes(4, p0) < ws
 
 
 def test_workspace_size_grows_with_m():

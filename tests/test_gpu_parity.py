@@ -169,6 +169,18 @@ def test_fwd_ragged_and_rank0():
         _fwd_checks(xbits, codes, scales, upb, dnb, g, tag=f"m{m} n{n} k{k} g{g} r{rank}")
 
 
+def test_fwd_small_m_tiles():
+    # the small-M contraction with one, two and four 16-row tiles, K slices
+    # that are and are not whole multiples of its prefetch step, ragged N
+    rng = np.random.default_rng(11)
+    from synth import gen_activations
+    for k in (1280, 2048):
+        codes, scales, upb, dnb = gen_payload(rng, 200, k, 32, 32)
+        xbits = gen_activations(rng, 64, k, 0.01)
+        for m in (1, 17, 32, 33, 64):
+            _fwd_checks(xbits[:m], codes, scales, upb, dnb, 32, tag=f"m{m} n200 k{k}")
+
+
 def test_fwd_zero_rows_and_large_activations():
     import w4_gemm_amd as W
     rng = np.random.default_rng(6)
@@ -199,6 +211,80 @@ def test_determinism(tiny):
     assert torch.equal(a, b) and torch.equal(ra.view(torch.int16), rb.view(torch.int16))
     assert torch.equal(q1.codes, q2.codes) and torch.equal(f1, f2)
     assert torch.equal(q1.scales.view(torch.int16), q2.scales.view(torch.int16))
+
+
+# ------------------------------------------------------------------ input gradient
+def _dgrad_checks(dybits, codes, scales, upb, dnb, group, rows=None, tag=""):
+    import w4_gemm_amd as W
+    p = to_dev_payload(codes, scales, upb, dnb, group)
+    dyd = _x_dev(dybits)
+    d32 = W.linear_dgrad(dyd, p, torch.float32)
+    d16 = W.linear_dgrad(dyd, p, torch.bfloat16)
+    torch.cuda.synchronize()
+    d32h = d32.cpu().numpy().astype(np.float64)
+    d16h = bf16_tensor_to_f64(d16)
+    assert np.all(np.isfinite(d32h))
+    assert np.array_equal(d16h, O.bf16_round(d32h))
+    rows = np.arange(dybits.shape[0]) if rows is None else rows
+    dy = O.bf16_decode(dybits[rows])
+    q, s, up, dn = payload_fp64(codes, scales, upb, dnb)
+    ref = O.dgrad(dy, q, s, up, dn, group)
+    diag = O.dgrad_fp16_operands(dy, q, s, up, dn, group)
+    got = d32h[rows]
+    e, cs, ed = O.rel_fro(got, ref), O.cosine(got, ref), O.rel_fro(got, diag)
+    print(f"{tag}: dgrad relF={e:.3e} cos={cs:.7f} vs-fp16-operands={ed:.3e}")
+    assert e <= Y_TOL and cs >= COS_TOL and ed <= DIAG_TOL
+    return d32h
+
+
+def _gen_dy(rng, m, n):
+    from synth import f32_to_bf16_bits
+    dy = rng.standard_normal((m, n)).astype(np.float32)
+    if m > 4:
+        dy[1] = 0.0                # an all-zero row
+        dy[2] *= 1e-6              # a small-gradient row (the fp16 row factor matters)
+        dy[3] *= 3.0e4             # a large one
+    return f32_to_bf16_bits(dy)
+
+
+def test_dgrad_tiny(tiny):
+    t = tiny
+    dyb = _gen_dy(np.random.default_rng(21), t["cfg"].M, t["cfg"].N)
+    _dgrad_checks(dyb, t["codes"], t["scales"], t["upb"], t["dnb"], 32, tag="cfg1")
+
+
+def test_dgrad_ragged_ranks_groups():
+    rng = np.random.default_rng(22)
+    for (m, n, k, g, rank) in [(100, 192, 768, 64, 32), (3, 64, 256, 32, 0), (130, 128, 512, 32, 64),
+                               (257, 320, 1024, 64, 32)]:
+        codes, scales, upb, dnb = gen_payload(rng, n, k, g, max(rank, 1))
+        if rank == 0:
+            upb = dnb = None
+        _dgrad_checks(_gen_dy(rng, m, n), codes, scales, upb, dnb, g,
+                      tag=f"m{m} n{n} k{k} g{g} r{rank}")
+
+
+def test_dgrad_determinism_and_empty(tiny):
+    import w4_gemm_amd as W
+    t = tiny
+    p = to_dev_payload(t["codes"], t["scales"], t["upb"], t["dnb"], 32)
+    dyd = _x_dev(_gen_dy(np.random.default_rng(23), 64, t["cfg"].N))
+    a = W.linear_dgrad(dyd, p); b = W.linear_dgrad(dyd, p)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    W.linear_dgrad(torch.empty((0, t["cfg"].N), dtype=torch.bfloat16, device=dev()), p,
+                   out=torch.empty((0, t["cfg"].K), device=dev()))
+
+
+@pytest.mark.parametrize("cfg_id", [2, 4, 5])
+def test_dgrad_full_size_sampled(cfg_id):
+    cfg = CONFIGS[cfg_id]
+    rng = np.random.default_rng(300 + cfg_id)
+    codes, scales, upb, dnb = gen_payload(rng, cfg.N, cfg.K, cfg.group, cfg.rank)
+    dyb = _gen_dy(np.random.default_rng(cfg_id), cfg.M, cfg.N)
+    rows = np.sort(np.concatenate([[1, 2, 3], np.random.default_rng(7).choice(
+        np.arange(4, cfg.M), 21, replace=False)]))
+    _dgrad_checks(dyb, codes, scales, upb, dnb, cfg.group, rows=rows, tag=f"cfg{cfg_id}")
 
 
 # ------------------------------------------------------------------ full-size shapes

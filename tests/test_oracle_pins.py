@@ -312,6 +312,34 @@ def pin_forward_consistent():
     assert O.rel_fro(yd, O.forward(x * 3000, q, s, up, dn, g)) < 2e-3
 
 
+def pin_dgrad_adjoint():
+    # the input gradient is the adjoint of the forward: <dy, f(x)> = <g(dy), x>
+    # for every x and dy, and it equals dy @ W_hat built explicitly
+    rng = np.random.default_rng(14)
+    n, k, g, m = 40, 768, 32, 5
+    q, s, up, dn = _payload(rng, n, k, g, 32)
+    x = rng.standard_normal((m, k))
+    dy = rng.standard_normal((m, n))
+    dx = O.dgrad(dy, q, s, up, dn, g)
+    lhs = np.sum(dy * O.forward(x, q, s, up, dn, g))
+    rhs = np.sum(dx * x)
+    assert abs(lhs - rhs) <= 1e-12 * np.linalg.norm(dy) * np.linalg.norm(x) * np.linalg.norm(
+        O.reconstruct(q, s, up, dn, g))
+    np.testing.assert_allclose(dx, dy @ O.reconstruct(q, s, up, dn, g), rtol=1e-12, atol=1e-13)
+    # one output feature, one K block, rank 0: dx is that weight row scaled
+    e = np.zeros((1, n)); e[0, 3] = 2.0
+    row = O.dgrad(e, q, s, up[:, :0], dn[:, :0], g)
+    w0 = O.rotate(q[3:4] * np.repeat(s[3:4], g, 1))
+    np.testing.assert_allclose(row, 2.0 * w0, atol=1e-14)
+    # fp16-operand diagnostic: exact on fp16-exact operands, close otherwise
+    dyi = rng.integers(-3, 4, (m, n)).astype(float)
+    si = np.full((n, k // g), 2.0 ** -7)
+    np.testing.assert_allclose(O.dgrad_fp16_operands(dyi, q, si, up, dn, g),
+                               O.dgrad(dyi, q, si, up, dn, g), rtol=1e-12, atol=1e-12)
+    dd = O.dgrad_fp16_operands(dy * 1e-6, q, s, up, dn, g)
+    assert O.rel_fro(dd, O.dgrad(dy * 1e-6, q, s, up, dn, g)) < 2e-3
+
+
 def pin_low_rank_weight():
     rng = np.random.default_rng(11)
     n, k = 128, 512
@@ -410,6 +438,14 @@ def _mutations():
     def dropped_lowrank(x, q, scale, up, down, group):
         return orig_fwd(x, q, scale, up[:, :0], down[:, :0], group)
 
+    def dgrad_unrotated(dy, q, scale, up, down, group):
+        dy = np.asarray(dy, float)
+        return dy @ orig_dequant(q, scale, group) + (dy @ up) @ down.T
+
+    def dgrad_swapped_factors(dy, q, scale, up, down, group):
+        dy = np.asarray(dy, float)
+        return O.rotate(dy @ orig_dequant(q, scale, group)) + (dy @ up[:, ::-1]) @ down.T
+
     def swapped_nibbles(q):
         q = np.asarray(q).astype(np.int64)
         return ((q[..., 1::2] & 0xF) | ((q[..., 0::2] & 0xF) << 4)).astype(np.uint8)
@@ -429,6 +465,8 @@ def _mutations():
         ("codes_for_scale", symmetric_clamp),
         ("dequant", tiled_groups),
         ("forward", dropped_lowrank),
+        ("dgrad", dgrad_unrotated),
+        ("dgrad", dgrad_swapped_factors),
         ("pack", swapped_nibbles),
         ("candidate_scale_exact", fraction_off_by_one),
         ("svd_init", svd_no_sqrt),

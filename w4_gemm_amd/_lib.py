@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "SQ_OK", 1: "SQ_E_NULL", 2: "SQ_E_SHAPE", 3: "SQ_E_GROUP", 4:
 # every symbol include/sq.h declares
 EXPORTS = ("sq_quantize_weight", "sq_linear_fwd_workspace_bytes", "sq_linear_fwd",
            "sq_linear_fwd_rotate", "sq_linear_fwd_contract", "sq_reconstruct_bf16",
-           "sq_status_str", "sq_abi_version")
+           "sq_linear_dgrad_workspace_bytes", "sq_linear_dgrad", "sq_status_str",
+           "sq_abi_version")
 
 
 class SqW4(ctypes.Structure):
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.sq_linear_fwd_contract.argtypes = [i64, ctypes.POINTER(SqW4), vp, ctypes.c_int, vp,
                                              ctypes.c_size_t, vp]
         L.sq_linear_fwd_contract.restype = ctypes.c_int
+        L.sq_linear_dgrad_workspace_bytes.argtypes = [i64, ctypes.POINTER(SqW4)]
+        L.sq_linear_dgrad_workspace_bytes.restype = ctypes.c_size_t
+        L.sq_linear_dgrad.argtypes = [vp, i64, ctypes.POINTER(SqW4), vp, ctypes.c_int, vp,
+                                      ctypes.c_size_t, vp]
+        L.sq_linear_dgrad.restype = ctypes.c_int
         L.sq_reconstruct_bf16.argtypes = [ctypes.POINTER(SqW4), vp, vp]
         L.sq_reconstruct_bf16.restype = ctypes.c_int
         L.sq_status_str.argtypes = [ctypes.c_int]
@@ -111,3 +117,13 @@ def sq_linear_fwd_contract(m: int, p: SqW4, y, y_dtype: int, workspace, workspac
 
 def sq_reconstruct_bf16(p: SqW4, w_hat, stream) -> int:
     return lib().sq_reconstruct_bf16(ctypes.byref(p), w_hat, stream)
+
+
+def sq_linear_dgrad_workspace_bytes(m: int, p: SqW4) -> int:
+    return lib().sq_linear_dgrad_workspace_bytes(m, ctypes.byref(p))
+
+
+def sq_linear_dgrad(dy, m: int, p: SqW4, dx, dx_dtype: int, workspace, workspace_bytes: int,
+                    stream) -> int:
+    return lib().sq_linear_dgrad(dy, m, ctypes.byref(p), dx, dx_dtype, workspace,
+                                 workspace_bytes, stream)

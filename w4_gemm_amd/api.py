@@ -130,6 +130,30 @@ def linear_fwd_contract(m: int, p: W4Payload, out: torch.Tensor, workspace: torc
     return out
 
 
+def dgrad_workspace_bytes(m: int, p: W4Payload) -> int:
+    return _lib.sq_linear_dgrad_workspace_bytes(m, p.abi())
+
+
+def linear_dgrad(dy: torch.Tensor, p: W4Payload, out_dtype=torch.float32,
+                 workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """sq_linear_dgrad: bf16 dy [M,N] -> dx = dy @ W_hat [M,K] (fp32 or bf16)."""
+    _require(dy, torch.bfloat16, "dy")
+    m = dy.shape[0]
+    if out is None:
+        out = torch.empty((m, p.k), dtype=out_dtype, device=dy.device)
+    _require(out, out.dtype, "out")
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (m, p.k):
+        raise ValueError("out must be fp32 or bf16 of shape [M, K]")
+    dt = SQ_BF16 if out.dtype == torch.bfloat16 else SQ_F32
+    nbytes = dgrad_workspace_bytes(m, p)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dy.device)
+    _check(_lib.sq_linear_dgrad(dy.data_ptr(), m, p.abi(), out.data_ptr(), dt,
+                                workspace.data_ptr(), workspace.numel(), _stream()),
+           "sq_linear_dgrad")
+    return out
+
+
 def reconstruct_bf16(p: W4Payload, out: torch.Tensor | None = None):
     """sq_reconstruct_bf16: payload -> bf16 W_hat [N,K]."""
     if out is None:

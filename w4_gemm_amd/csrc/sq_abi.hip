@@ -55,11 +55,12 @@ const char* sq_status_str(sq_status_t s) {
   switch (s) {
     case SQ_OK: return "ok";
     case SQ_E_NULL: return "a required pointer is NULL";
-    case SQ_E_SHAPE: return "bad shape: need K % 256 == 0, K >= 256, N >= 1, M >= 0";
+    case SQ_E_SHAPE:
+      return "bad shape: need K % 256 == 0, K >= 256, N >= 1, M >= 0 (input gradient: N % 64 == 0)";
     case SQ_E_GROUP: return "group must be 32 or 64";
     case SQ_E_RANK: return "rank must be 0, 32 or 64";
     case SQ_E_ALIGN: return "every pointer must be 16-byte aligned";
-    case SQ_E_WORKSPACE: return "workspace smaller than sq_linear_fwd_workspace_bytes()";
+    case SQ_E_WORKSPACE: return "workspace smaller than the entry point's *_workspace_bytes()";
     case SQ_E_DTYPE: return "output dtype must be SQ_F32 or SQ_BF16";
     case SQ_E_ARCH: return "the current device is not gfx950 (MI355X)";
     case SQ_E_HIP: return "a HIP runtime call or kernel launch failed";
@@ -138,6 +139,30 @@ sq_status_t sq_linear_fwd(const uint16_t* x, int64_t m, const sq_w4_t* p, void* 
     return st;
   return from_hip(sq::launch_fwd_contract(plan, p->codes, p->scales, p->lora_up, y,
                                           y_dtype == SQ_BF16, workspace, s));
+}
+
+size_t sq_linear_dgrad_workspace_bytes(int64_t m, const sq_w4_t* p) {
+  if (!p || m <= 0 || p->k < 256 || p->k % 256 || p->n < 64 || p->n % 64) return 0;
+  if (p->rank != 0 && p->rank != 32 && p->rank != 64) return 0;
+  return sq::plan_dgrad(m, p->n, p->k, p->group, p->rank).total;
+}
+
+sq_status_t sq_linear_dgrad(const uint16_t* dy, int64_t m, const sq_w4_t* p, void* dx,
+                            sq_dtype_t dx_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (dx_dtype != SQ_F32 && dx_dtype != SQ_BF16) return SQ_E_DTYPE;
+  sq_status_t st = check_payload(p, true);
+  if (st != SQ_OK) return st;
+  if (m < 0 || p->n % 64 != 0) return SQ_E_SHAPE;
+  if (m == 0) return SQ_OK;
+  if (!dy || !dx || !workspace) return SQ_E_NULL;
+  if (!aligned16(dy) || !aligned16(dx) || !aligned16(workspace)) return SQ_E_ALIGN;
+  const sq::DgradPlan plan = sq::plan_dgrad(m, p->n, p->k, p->group, p->rank);
+  if (workspace_bytes < plan.total) return SQ_E_WORKSPACE;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_dgrad(plan, dy, p->codes, p->scales, p->lora_up, p->lora_down, dx,
+                                   dx_dtype == SQ_BF16, workspace,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 sq_status_t sq_reconstruct_bf16(const sq_w4_t* p, uint16_t* w_hat, void* stream) {

@@ -47,6 +47,46 @@ __device__ __forceinline__ float fp16_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
+// Smallest e with a <= 2^e for the bf16 magnitude bits `mx` (0 for a zero
+// row), floored at -100.
+__device__ __forceinline__ int row_exponent(uint32_t mx) {
+  const float a = bf16_to_f32(mx);
+  int e = 0;
+  if (a > 0.0f) {
+    int ex;
+    const float mant = frexpf(a, &ex);   // a = mant * 2^ex, mant in [0.5, 1)
+    e = (mant == 0.5f) ? ex - 1 : ex;
+  }
+  return max(e, -100);
+}
+
+// ---------------------------------------------------------------------------
+// Tiled contractions (forward and input gradient)
+// ---------------------------------------------------------------------------
+// Map the linear workgroup id to a tile.  Ids congruent mod 8 are dispatched
+// to the same XCD, so each XCD gets one contiguous run of tile numbers; within
+// the run the numbers walk XCD_GROUP_M tile rows down before stepping one tile
+// column across, so the ~32 workgroups resident on an XCD at a time cover a
+// 4 x 8 block of tiles and share both operands in its L2 (4 A strips + 8 B
+// strips instead of 1 + 32).
+constexpr int64_t XCD_GROUP_M = 4;
+__device__ __forceinline__ void xcd_tile(int64_t lin, int64_t tiles, int64_t nt, int64_t& tm,
+                                         int64_t& tn) {
+  const int64_t xcd = lin & 7, idx = lin >> 3;
+  const int64_t per = tiles >> 3, rem = tiles & 7;
+  const int64_t t = xcd * per + min(xcd, rem) + idx;
+  const int64_t mt = tiles / nt;
+  const int64_t grp = t / (XCD_GROUP_M * nt), first = grp * XCD_GROUP_M;
+  const int64_t gsz = min(XCD_GROUP_M, mt - first);
+  const int64_t w = t - grp * XCD_GROUP_M * nt;
+  tm = first + w % gsz;
+  tn = w / gsz;
+}
+
+// Slot of 16-byte chunk c in row r is c ^ a_swz(r): the 16 rows read by one
+// fragment load land in distinct bank groups whether the LDS has 32 or 64 banks.
+__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 // ---------------------------------------------------------------------------
 // Hadamard-256 butterflies in the 16-rows x 256-columns wave layout.
 // Unnormalized: after both halves every lane holds S @ v for its block slice,

@@ -64,19 +64,6 @@ __device__ __forceinline__ void load_x64(uint32_t (&xb)[32], const uint16_t* __r
   }
 }
 
-// Smallest e with a <= 2^e for the bf16 magnitude bits `mx` (0 for a zero
-// row), floored at -100.
-__device__ __forceinline__ int row_exponent(uint32_t mx) {
-  const float a = bf16_to_f32(mx);
-  int e = 0;
-  if (a > 0.0f) {
-    int ex;
-    const float mant = frexpf(a, &ex);   // a = mant * 2^ex, mant in [0.5, 1)
-    e = (mant == 0.5f) ? ex - 1 : ex;
-  }
-  return max(e, -100);
-}
-
 // Pass 1: grid (ceil(m/16), slices); slice q covers the 256-column blocks
 // [q*bps, q*bps + bps) and the workgroup's four waves take every fourth one.
 // Writes amax_part[q][row] (bf16 magnitude bits; they order like the values)
@@ -249,26 +236,6 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
 // K advances 64 values per pipeline stage (two 16x16x32 MFMA steps).
 constexpr int GBK = 64;
 
-// Map the linear workgroup id to a tile.  Ids congruent mod 8 are dispatched
-// to the same XCD, so each XCD gets one contiguous run of tile numbers; within
-// the run the numbers walk XCD_GROUP_M tile rows down before stepping one tile
-// column across, so the ~32 workgroups resident on an XCD at a time cover a
-// 4 x 8 block of tiles and share both operands in its L2 (4 A strips + 8 B
-// strips instead of 1 + 32).
-constexpr int64_t XCD_GROUP_M = 4;
-__device__ __forceinline__ void xcd_tile(int64_t lin, int64_t tiles, int64_t nt, int64_t& tm,
-                                         int64_t& tn) {
-  const int64_t xcd = lin & 7, idx = lin >> 3;
-  const int64_t per = tiles >> 3, rem = tiles & 7;
-  const int64_t t = xcd * per + min(xcd, rem) + idx;
-  const int64_t mt = tiles / nt;
-  const int64_t grp = t / (XCD_GROUP_M * nt), first = grp * XCD_GROUP_M;
-  const int64_t gsz = min(XCD_GROUP_M, mt - first);
-  const int64_t w = t - grp * XCD_GROUP_M * nt;
-  tm = first + w % gsz;
-  tn = w / gsz;
-}
-
 // ---------------------------------------------------------------- large-tile contraction
 // BM x 256 output tile per workgroup (BM = 256, 224 or 128), eight waves of
 // (BM/2) x 64 ((BM/32) x 4 MFMA tiles each, two waves per SIMD).
@@ -305,10 +272,6 @@ __shared__ __attribute__((aligned(16))) uint8_t big_b0[BIG_TILE_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t big_b1[BIG_TILE_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t big_s0[BIG_S_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t big_s1[BIG_S_BYTES];
-
-// Slot of 16-byte chunk c in row r is c ^ a_swz(r): the 16 rows read by one
-// fragment load land in distinct bank groups whether the LDS has 32 or 64 banks.
-__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // 8 packed codes -> fp16(q*s) pairs in the permuted K order.  Per pair the
 // nibbles are selected, their sign bit flipped (q + 8) and the fp16 exponent

@@ -32,4 +32,18 @@ hipError_t launch_fwd_contract(const FwdPlan& plan, const uint8_t* codes, const 
                                const uint16_t* up, void* y, int y_bf16, void* workspace,
                                hipStream_t stream);
 
+// Input gradient: workspace layout and launch.
+struct DgradPlan {
+  int64_t m, n, k;
+  int group, rank;
+  int stats_sps, stats_slices;   // 32-column steps of N per statistics slice, slices
+  size_t off_upT, off_amax, off_tpart, off_dy16, off_thi, off_tlo, off_rowscale, off_hdhi,
+      off_hdlo, off_c, total;
+};
+DgradPlan plan_dgrad(int64_t m, int64_t n, int64_t k, int group, int rank);
+
+hipError_t launch_dgrad(const DgradPlan& plan, const uint16_t* dy, const uint8_t* codes,
+                        const uint16_t* scales, const uint16_t* up, const uint16_t* down,
+                        void* dx, int dx_bf16, void* workspace, hipStream_t stream);
+
 }  // namespace sq
