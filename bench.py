@@ -22,7 +22,8 @@ profiles/; it is null when the kernel source has changed since then.
 `cpu_baseline` is the CPU oracle's forward on a sample of rows, on this
 host's cores.
 
-Extra fields: the small-M forward sweep (M = 1, 16, 128 on the
+Extra fields: the input gradient (sq_linear_dgrad, dx = dy W_hat, same
+flop count as the forward, not part of the step), the small-M forward sweep (M = 1, 16, 128 on the
 6144x16384 g32 weight) in GB/s of bytes the call must move, and the
 rotation, reconstruct and quantize kernels against HBM peak.
 
@@ -83,7 +84,7 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--ops", default="fwd,reconstruct,quantize,smallm,configs")
+    ap.add_argument("--ops", default="fwd,reconstruct,quantize,dgrad,smallm,configs")
     ap.add_argument("--small-m", default="1,16,128")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -164,6 +165,22 @@ def main():
             b.record()
         torch.cuda.synchronize()
         res["reconstruct"] = np.array([a.elapsed_time(b) for a, b in marks])
+    # ---------------------------------------------------------------- input gradient
+    if "dgrad" in ops:
+        gen = torch.Generator(device=dev).manual_seed(0)
+        dy = torch.randn((M, N), generator=gen, device=dev).to(torch.bfloat16)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dws = torch.empty(W.dgrad_workspace_bytes(M, p0), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            W.linear_dgrad(dy, p0, out=dx, workspace=dws)
+        marks = [(ev(), ev()) for _ in range(args.steps)]
+        for a, b in marks:
+            a.record()
+            W.linear_dgrad(dy, p0, out=dx, workspace=dws)
+            b.record()
+        torch.cuda.synchronize()
+        res["dgrad"] = np.array([a.elapsed_time(b) for a, b in marks])
+        del dy, dx, dws
     # ---------------------------------------------------------------- quantize
     if "quantize" in ops:
         qp = W.empty_payload(N, K, G, R, dev)
@@ -234,6 +251,11 @@ def main():
         ms_step += t
         out.update(quantize_ms=t, quantize_gbps=quant_bytes / (t * 1e-3) / 1e9)
         out["quantize_pct_hbm_peak"] = 100.0 * out["quantize_gbps"] / PEAK_HBM_GBPS
+    if "dgrad" in res:
+        t = float(np.mean(res["dgrad"]))
+        out.update(dgrad_ms=t, dgrad_ms_median=float(np.median(res["dgrad"])),
+                   dgrad_tflops=flops_fwd / (t * 1e-3) / 1e12)
+        out["dgrad_pct_bf16_mfma_peak"] = 100.0 * out["dgrad_tflops"] / PEAK_F16_TFLOPS
     if "smallm" in res:
         out["fwd_small_m"] = res["smallm"]
     if "configs" in res:

@@ -37,6 +37,7 @@ struct DgradPlan {
   int64_t m, n, k;
   int group, rank;
   int stats_sps, stats_slices;   // 32-column steps of N per statistics slice, slices
+  int tile_m;                    // rows of the contraction tile (256 or 224)
   size_t off_upT, off_amax, off_tpart, off_dy16, off_thi, off_tlo, off_rowscale, off_hdhi,
       off_hdlo, off_c, total;
 };
