@@ -23,7 +23,8 @@ profiles/; it is null when the kernel source has changed since then.
 host's cores.
 
 Extra fields: the input gradient (sq_linear_dgrad, dx = dy W_hat, same
-flop count as the forward, not part of the step), the small-M forward sweep (M = 1, 16, 128 on the
+flop count as the forward, not part of the step), the streaming builder's
+wall time on a two-layer fp32 checkpoint, the small-M forward sweep (M = 1, 16, 128 on the
 6144x16384 g32 weight) in GB/s of bytes the call must move, and the
 rotation, reconstruct and quantize kernels against HBM peak.
 
@@ -84,7 +85,7 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--ops", default="fwd,reconstruct,quantize,dgrad,smallm,configs")
+    ap.add_argument("--ops", default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs")
     ap.add_argument("--small-m", default="1,16,128")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -202,6 +203,9 @@ def main():
             b.record()
         torch.cuda.synchronize()
         res["quantize"] = np.array([a.elapsed_time(b) for a, b in marks])
+    # ---------------------------------------------------------------- streaming builder
+    if "builder" in ops:
+        res["builder"] = builder_run(torch, dev)
     # ---------------------------------------------------------------- other shapes
     if "configs" in ops:
         res["configs"] = other_configs(torch, W, dev, [2, 3, 5], max(5, args.steps // 5),
@@ -256,6 +260,8 @@ def main():
         out.update(dgrad_ms=t, dgrad_ms_median=float(np.median(res["dgrad"])),
                    dgrad_tflops=flops_fwd / (t * 1e-3) / 1e12)
         out["dgrad_pct_bf16_mfma_peak"] = 100.0 * out["dgrad_tflops"] / PEAK_F16_TFLOPS
+    if "builder" in res:
+        out["builder"] = res["builder"]
     if "smallm" in res:
         out["fwd_small_m"] = res["smallm"]
     if "configs" in res:
@@ -312,6 +318,36 @@ def copy_calibration(torch, dev, reps=5):
     print(json.dumps({"calibration_copy_bytes_read": COPY_BYTES, "calibration_copy_bytes_written":
                       COPY_BYTES, "blit_ms": dt * 1e3, "elementwise_ms": dt2 * 1e3}), flush=True)
     return 0
+
+
+def builder_run(torch, dev):
+    """The streaming builder end to end on a synthetic two-layer checkpoint
+    (the MLP-up and MLP-down weights, fp32, 16384x6144 and 6144x16384 g32
+    rank 32, randomized SVD) in a temporary directory: wall seconds and
+    source GB/s, SVD, quantizer and file writes included."""
+    import shutil
+    import tempfile
+
+    from safetensors.torch import save_file
+
+    from w4_gemm_amd import builder as B
+    from synth import gen_weight
+    tmp = tempfile.mkdtemp(prefix="sq_builder_")
+    try:
+        rng = np.random.default_rng(0)
+        src = os.path.join(tmp, "model.safetensors")
+        save_file({"mlp.up.weight": torch.from_numpy(gen_weight(rng, 16384, 6144, 8)),
+                   "mlp.down.weight": torch.from_numpy(gen_weight(rng, 6144, 16384, 8))}, src)
+        src_bytes = os.path.getsize(src)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        out = B.build(src, os.path.join(tmp, "slab"), rank=32, group=32, svd="randomized")
+        dt = time.perf_counter() - t
+        return {"seconds": dt, "source_bytes": src_bytes, "slab_bytes": os.path.getsize(out),
+                "source_gbps": src_bytes / dt / 1e9,
+                "workload": "2 fp32 weights 16384x6144 + 6144x16384, g32 rank 32"}
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
 
 
 def layer(torch, W, dev, cfg_id):
