@@ -47,6 +47,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+PEAK_VALU_TOPS = 39.32        # non-packed vector lane-ops: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+SWEEP_OPS_PER_ELEMENT = 31 * 5
 # counter summary of the contraction kernel at 4480x16384x6144 (see its header)
 GEMM_PMC = os.path.join(ROOT, "profiles", "k_fwd_gemm_big_mlp-up_4480x16384x6144_pmc.txt")
 GEMM_SRC = os.path.join(ROOT, "w4_gemm_amd", "csrc", "sq_fwd.hip")
@@ -255,6 +257,13 @@ def main():
         ms_step += t
         out.update(quantize_ms=t, quantize_gbps=quant_bytes / (t * 1e-3) / 1e9)
         out["quantize_pct_hbm_peak"] = 100.0 * out["quantize_gbps"] / PEAK_HBM_GBPS
+        # the 31-candidate sweep is plain fp32 ALU work: 5 lane-ops per element
+        # and candidate (multiply, round, clamp, two FMAs), against the
+        # non-packed vector issue rate of 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+        alu = SWEEP_OPS_PER_ELEMENT * N * K / (t * 1e-3)
+        out["quantize_alu"] = {"bound": "alu", "achieved": alu / 1e12, "peak": PEAK_VALU_TOPS,
+                               "unit": "Tlane-op/s", "frac": alu / 1e12 / PEAK_VALU_TOPS,
+                               "ops_per_element": SWEEP_OPS_PER_ELEMENT}
     if "dgrad" in res:
         t = float(np.mean(res["dgrad"]))
         out.update(dgrad_ms=t, dgrad_ms_median=float(np.median(res["dgrad"])),
