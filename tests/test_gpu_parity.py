@@ -181,6 +181,48 @@ def test_fwd_small_m_tiles():
             _fwd_checks(xbits[:m], codes, scales, upb, dnb, 32, tag=f"m{m} n200 k{k}")
 
 
+def test_fwd_decode_shapes():
+    # the M <= 16 path: K slices of 512 and 1024 values, whole and with a
+    # one-block last slice; N ragged against its 256-row workgroups and its
+    # 64-row waves; both group sizes; ranks 0, 32 and 64
+    rng = np.random.default_rng(12)
+    from synth import gen_activations
+    for (n, k, g, rank) in [(200, 256, 32, 32), (300, 768, 64, 64), (256, 1280, 32, 0),
+                            (520, 3328, 32, 32), (64, 2048, 64, 32), (1, 512, 32, 32)]:
+        codes, scales, upb, dnb = gen_payload(rng, n, k, g, max(rank, 1))
+        if rank == 0:
+            upb = dnb = None
+        xbits = gen_activations(rng, 16, k, 0.01)
+        for m in (1, 2, 5, 16):
+            _fwd_checks(xbits[:m], codes, scales, upb, dnb, g, tag=f"m{m} n{n} k{k} g{g} r{rank}")
+
+
+def test_fwd_decode_split_calls_and_slices_apart():
+    # rotate + contract on one workspace equals the one-call forward bit for
+    # bit; a row whose K slices differ in scale by 1e8 keeps both (each slice
+    # has its own power of two)
+    import w4_gemm_amd as W
+    rng = np.random.default_rng(13)
+    codes, scales, upb, dnb = gen_payload(rng, 300, 2048, 32, 32)
+    from synth import f32_to_bf16_bits
+    x = rng.standard_normal((16, 2048)).astype(np.float32)
+    x[3, :512] *= 1e4
+    x[3, 512:] *= 1e-4
+    x[5, 1024:] = 0.0
+    xbits = f32_to_bf16_bits(x)
+    p = to_dev_payload(codes, scales, upb, dnb, 32)
+    for m in (1, 4, 16):
+        _fwd_checks(xbits[:m], codes, scales, upb, dnb, 32, tag=f"slices apart m{m}")
+        xd = _x_dev(xbits[:m])
+        ws = torch.empty(W.fwd_workspace_bytes(m, p), dtype=torch.uint8, device=dev())
+        y1 = W.linear_fwd(xd, p, torch.float32, workspace=ws)
+        y2 = torch.empty_like(y1)
+        W.linear_fwd_rotate(xd, p, ws)
+        W.linear_fwd_contract(m, p, y2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+
+
 def test_fwd_zero_rows_and_large_activations():
     import w4_gemm_amd as W
     rng = np.random.default_rng(6)

@@ -80,9 +80,15 @@ sq_status_t sq_quantize_weight(const float* w, const sq_w4_t* p, uint8_t* fidx,
                                       static_cast<hipStream_t>(stream)));
 }
 
+static sq::FwdPlan make_fwd_plan(int64_t m, const sq_w4_t* p) {
+  if (sq::decode_eligible(m, p->n, p->k, p->rank))
+    return sq::plan_decode(m, p->n, p->k, p->group, p->rank);
+  return sq::plan_fwd(m, p->n, p->k, p->group, p->rank);
+}
+
 size_t sq_linear_fwd_workspace_bytes(int64_t m, const sq_w4_t* p) {
   if (!p || m <= 0 || p->k < 256 || p->k % 256 || p->n < 1) return 0;
-  return sq::plan_fwd(m, p->n, p->k, p->group, p->rank).total;
+  return make_fwd_plan(m, p).total;
 }
 
 static sq_status_t check_fwd(int64_t m, const sq_w4_t* p, void* workspace, size_t ws_bytes,
@@ -93,7 +99,7 @@ static sq_status_t check_fwd(int64_t m, const sq_w4_t* p, void* workspace, size_
   if (m == 0) return SQ_OK;
   if (!workspace) return SQ_E_NULL;
   if (!aligned16(workspace)) return SQ_E_ALIGN;
-  *plan = sq::plan_fwd(m, p->n, p->k, p->group, p->rank);
+  *plan = make_fwd_plan(m, p);
   if (ws_bytes < plan->total) return SQ_E_WORKSPACE;
   return SQ_OK;
 }
@@ -106,6 +112,9 @@ sq_status_t sq_linear_fwd_rotate(const uint16_t* x, int64_t m, const sq_w4_t* p,
   if (!x) return SQ_E_NULL;
   if (!aligned16(x)) return SQ_E_ALIGN;
   if ((st = check_device()) != SQ_OK) return st;
+  if (plan.dec)
+    return from_hip(sq::launch_decode_prep(plan, x, p->lora_down, workspace,
+                                           static_cast<hipStream_t>(stream)));
   return from_hip(sq::launch_fwd_rotate(plan, x, p->lora_down, workspace,
                                         static_cast<hipStream_t>(stream)));
 }
@@ -119,6 +128,10 @@ sq_status_t sq_linear_fwd_contract(int64_t m, const sq_w4_t* p, void* y, sq_dtyp
   if (!y) return SQ_E_NULL;
   if (!aligned16(y)) return SQ_E_ALIGN;
   if ((st = check_device()) != SQ_OK) return st;
+  if (plan.dec)
+    return from_hip(sq::launch_decode_contract(plan, nullptr, nullptr, p->codes, p->scales,
+                                               p->lora_up, y, y_dtype == SQ_BF16, workspace,
+                                               static_cast<hipStream_t>(stream)));
   return from_hip(sq::launch_fwd_contract(plan, p->codes, p->scales, p->lora_up, y,
                                           y_dtype == SQ_BF16, workspace,
                                           static_cast<hipStream_t>(stream)));
@@ -135,6 +148,9 @@ sq_status_t sq_linear_fwd(const uint16_t* x, int64_t m, const sq_w4_t* p, void* 
   if (!aligned16(x) || !aligned16(y)) return SQ_E_ALIGN;
   if ((st = check_device()) != SQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.dec)
+    return from_hip(sq::launch_decode_contract(plan, x, p->lora_down, p->codes, p->scales,
+                                               p->lora_up, y, y_dtype == SQ_BF16, workspace, s));
   if ((st = from_hip(sq::launch_fwd_rotate(plan, x, p->lora_down, workspace, s))) != SQ_OK)
     return st;
   return from_hip(sq::launch_fwd_contract(plan, p->codes, p->scales, p->lora_up, y,

@@ -22,9 +22,23 @@ struct FwdPlan {
   int skinny_mt;       // > 0: the small-M kernel with this many 16-row tiles
   int skinny_kslice;   // its K slice (a multiple of 256)
   int pre_bps, pre_slices;  // 256-column blocks per K slice of the statistics pass, slices
+  int dec;             // 1: the small-M decode path (rotation inside the contraction)
+  int dec_kslice;      // its K slice (a multiple of 256, at most 1024)
   size_t off_xh, off_thi, off_tlo, off_rowscale, off_downT, off_amax, off_tpart, off_partial, total;
 };
 FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank);
+
+// Small-M decode path (M <= 16): eligibility, plan and launches.  The whole
+// product runs in launch_decode_contract; in the split-call form the first
+// half stages x and lora_down in the workspace (launch_decode_prep) and the
+// second passes x = down = null to read them there.
+bool decode_eligible(int64_t m, int64_t n, int64_t k, int rank);
+FwdPlan plan_decode(int64_t m, int64_t n, int64_t k, int group, int rank);
+hipError_t launch_decode_prep(const FwdPlan& plan, const uint16_t* x, const uint16_t* down,
+                              void* workspace, hipStream_t stream);
+hipError_t launch_decode_contract(const FwdPlan& plan, const uint16_t* x, const uint16_t* down,
+                                  const uint8_t* codes, const uint16_t* scales, const uint16_t* up,
+                                  void* y, int y_bf16, void* workspace, hipStream_t stream);
 
 hipError_t launch_fwd_rotate(const FwdPlan& plan, const uint16_t* x, const uint16_t* down,
                              void* workspace, hipStream_t stream);
