@@ -36,7 +36,12 @@ constexpr int DEC_MAX_M = 16;
 constexpr int DEC_NB_MAX = 4;                    // blocks per K slice at most
 constexpr int DEC_KS_MAX = 256 * DEC_NB_MAX;
 constexpr int DEC_XS = DEC_KS_MAX + 8;           // halves per LDS activation row (16 B pad)
-constexpr int DEC_DEPTH = 2;                     // blocks of codes in flight per wave
+// Blocks of codes in flight per wave.  One (the next block's loads go out
+// once the current block is contracted) measured fastest: with two waves
+// per SIMD the other wave covers the wait, and fewer requests in flight
+// keep the memory queues short and the waves' progress even (two or three
+// blocks ahead left some waves stalled at issue for microseconds).
+constexpr int DEC_DEPTH = 1;
 
 // s_waitcnt immediate: lgkmcnt(0), the other counters untouched.
 constexpr int DEC_WAIT_LGKM0 = 0xC07F;
@@ -396,6 +401,12 @@ __global__ void __launch_bounds__(256) k_decode_reduce(const float* __restrict__
   const int64_t row = blockIdx.y;
   const int64_t col = std::min((int64_t)blockIdx.x * 256 + tid, n - 1);
   const int64_t mn = m * n;
+  // the column's up row first, so that every load of the thread is in flight together
+  u32x4 urow[8];
+  const u32x4* usrc = reinterpret_cast<const u32x4*>(up + col * rank);
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    if (c < (rank >> 3)) urow[c] = usrc[c];
   float sum = 0.0f, t = 0.0f;
   for (int z0 = 0; z0 < splits; z0 += 16) {
     float pv[16], tv[16];
@@ -416,13 +427,13 @@ __global__ void __launch_bounds__(256) k_decode_reduce(const float* __restrict__
   __syncthreads();
   if ((int64_t)blockIdx.x * 256 + tid >= n) return;
   float lr = 0.0f;
-  const u32x4* urow = reinterpret_cast<const u32x4*>(up + col * rank);
-  for (int c = 0; c < (rank >> 3); ++c) {
-    const u32x4 u = urow[c];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    if (c >= (rank >> 3)) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      lr = __builtin_fmaf(s_t[8 * c + 2 * e], bf16_to_f32(u[e] & 0xFFFFu), lr);
-      lr = __builtin_fmaf(s_t[8 * c + 2 * e + 1], bf16_to_f32(u[e] >> 16), lr);
+      lr = __builtin_fmaf(s_t[8 * c + 2 * e], bf16_to_f32(urow[c][e] & 0xFFFFu), lr);
+      lr = __builtin_fmaf(s_t[8 * c + 2 * e + 1], bf16_to_f32(urow[c][e] >> 16), lr);
     }
   }
   const float out = sum + lr;
