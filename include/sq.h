@@ -113,6 +113,10 @@ sq_status_t sq_linear_fwd(const uint16_t *x, int64_t m, const sq_w4_t *p, void *
  *             activations, the row powers of two and the rank-r projection
  *             x @ lora_down.
  *   contract: reads that workspace and the payload; writes y.
+ * For m <= 16 the rotation and the projection run inside the contraction
+ * (the whole call streams the payload once from its first cycle): there
+ * rotate only copies x and p->lora_down into the workspace, and contract
+ * does the rest from those copies.
  * Both take the same m, p and workspace; contract must follow a rotate of the
  * same x on the same workspace (stream order suffices). */
 sq_status_t sq_linear_fwd_rotate(const uint16_t *x, int64_t m, const sq_w4_t *p, void *workspace,
