@@ -79,29 +79,6 @@ __device__ __forceinline__ void lane_stage16(float (&v)[16], int lane) {
     v[i] = __builtin_fmaf(sg, v[i], __int_as_float(lane_xor<CTRL, BIT>(__float_as_int(v[i]))));
 }
 
-// 8 packed codes -> fp16(q*s) pairs in the K order [0,4,1,5,2,6,3,7].  The
-// nibble pair p sits at bits 4p and 16 + 4p of the word.  Pairs 0 and 2 are
-// selected at bits 0..3 (with the sign bit flipped: q + 8) under the exponent
-// of 1024, giving 1032 + q; pairs 1 and 3 are selected at bits 4..7, giving
-// 1024 + 16 (q + 8), which one exact fma maps back to q.  Each product q*s is
-// rounded once.
-__device__ __forceinline__ half8 dequant8(uint32_t w, dec_half2 s2) {
-  const dec_half2 b1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const dec_half2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const dec_half2 m72 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  const uint32_t w8 = w >> 8;
-  const dec_half2 h0 = __builtin_bit_cast(dec_half2, (w & 0x000F000Fu) ^ 0x64086408u);
-  const dec_half2 h1 = __builtin_bit_cast(dec_half2, (w & 0x00F000F0u) ^ 0x64806480u);
-  const dec_half2 h2 = __builtin_bit_cast(dec_half2, (w8 & 0x000F000Fu) ^ 0x64086408u);
-  const dec_half2 h3 = __builtin_bit_cast(dec_half2, (w8 & 0x00F000F0u) ^ 0x64806480u);
-  const dec_half2 q0 = h0 - b1032, q2 = h2 - b1032;
-  const dec_half2 q1 = __builtin_elementwise_fma(h1, sixteenth, m72);
-  const dec_half2 q3 = __builtin_elementwise_fma(h3, sixteenth, m72);
-  return __builtin_bit_cast(
-      half8, (u32x4){__builtin_bit_cast(uint32_t, q0 * s2), __builtin_bit_cast(uint32_t, q1 * s2),
-                     __builtin_bit_cast(uint32_t, q2 * s2), __builtin_bit_cast(uint32_t, q3 * s2)});
-}
-
 // Hadamard-256 butterflies of one block row held as 16 lanes x 16 values
 // (lane l % 16 holds block positions 16(l%16) + 0..15), unnormalized.
 __device__ __forceinline__ void fwht16_lanes16(float (&v)[16], int lane) {
@@ -361,10 +338,9 @@ __global__ void __launch_bounds__(256) k_fwd_decode(
           const uint32_t sbits =
               GSHIFT == 5 ? (c ? sc[d][t] >> 16 : sc[d][t] & 0xFFFFu) : sc[d][t] & 0xFFFFu;
           const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sbits);
-          const dec_half2 s2 = {sv, sv};
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[e], dequant8(cw[d][t][c][e], s2),
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[e], dequant8_f16(cw[d][t][c][e], sv),
                                                             acc[t], 0, 0, 0);
         }
       }

@@ -61,6 +61,34 @@ __device__ __forceinline__ int row_exponent(uint32_t mx) {
 }
 
 // ---------------------------------------------------------------------------
+// 8 packed int4 codes -> fp16(q*s) in the K order [0,4,1,5,2,6,3,7].  Code k
+// of the 8 is nibble k of the word (two's complement), so nibble pair p sits
+// at bits 4p and 16 + 4p.  Pairs 0 and 2 are selected at bits 0..3 with the
+// sign bit flipped (q + 8) under the fp16 exponent of 1024, giving 1032 + q;
+// pairs 1 and 3 are selected at bits 4..7, giving 1024 + 16 (q + 8), which
+// one exact fma maps back to q.  Each product q*s is rounded once.  One
+// shift, four 3-input bit ops and eight packed fp16 ops per word.
+// ---------------------------------------------------------------------------
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ half8 dequant8_f16(uint32_t w, _Float16 s) {
+  const half2_t s2 = {s, s};
+  const half2_t b1032 = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t m72 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t w8 = w >> 8;
+  const half2_t h0 = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) ^ 0x64086408u);
+  const half2_t h1 = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) ^ 0x64806480u);
+  const half2_t h2 = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) ^ 0x64086408u);
+  const half2_t h3 = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) ^ 0x64806480u);
+  const half2_t q0 = h0 - b1032, q2 = h2 - b1032;
+  const half2_t q1 = __builtin_elementwise_fma(h1, sixteenth, m72);
+  const half2_t q3 = __builtin_elementwise_fma(h3, sixteenth, m72);
+  return __builtin_bit_cast(
+      half8, (u32x4){__builtin_bit_cast(uint32_t, q0 * s2), __builtin_bit_cast(uint32_t, q1 * s2),
+                     __builtin_bit_cast(uint32_t, q2 * s2), __builtin_bit_cast(uint32_t, q3 * s2)});
+}
+
+// ---------------------------------------------------------------------------
 // Tiled contractions (forward and input gradient)
 // ---------------------------------------------------------------------------
 // Map the linear workgroup id to a tile.  Ids congruent mod 8 are dispatched

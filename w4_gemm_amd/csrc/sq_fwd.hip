@@ -273,24 +273,6 @@ __shared__ __attribute__((aligned(16))) uint8_t big_b1[BIG_TILE_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t big_s0[BIG_S_BYTES];
 __shared__ __attribute__((aligned(16))) uint8_t big_s1[BIG_S_BYTES];
 
-// 8 packed codes -> fp16(q*s) pairs in the permuted K order.  Per pair the
-// nibbles are selected, their sign bit flipped (q + 8) and the fp16 exponent
-// of 1024 inserted by (w & 0x000F000F) ^ 0x64086408 (one 3-input bit op);
-// then (1024 + q + 8) - 1032 is exact and * s rounds once.
-__device__ __forceinline__ half8 dequant8_f16(uint32_t word, _Float16 s) {
-  const half2v sv = {s, s};
-  const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  uint32_t o[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t w = word >> (4 * p);
-    half2v h = __builtin_bit_cast(half2v, (w & 0x000F000Fu) ^ 0x64086408u);
-    h = (h - off) * sv;
-    o[p] = __builtin_bit_cast(uint32_t, h);
-  }
-  return __builtin_bit_cast(half8, (u32x4){o[0], o[1], o[2], o[3]});
-}
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in [3:0], expcnt [6:4], lgkmcnt [11:8])
