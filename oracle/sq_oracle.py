@@ -35,6 +35,9 @@ library primitives.  Points the page leaves open are decided as follows
   R6 the sweep minimises the sum of squared errors in the rotated domain;
      ties go to the lowest fraction index.
   R7 packing: byte b = (q[2b] & 0xF) | (q[2b+1] & 0xF) << 4, two's complement.
+
+The int8-residual mode (the page's "v3.1 - int8-residual mode" section) is at
+the end of the module, with its own readings W1-W5.
 """
 from __future__ import annotations
 
@@ -506,6 +509,211 @@ def check_device_quant(r, res: QuantResult, group: int, q_dev, scale_dev, fidx_d
         "groups": int(n * ng),
         "uncertified": int((~cert).sum()),
         "differ": int((~same).sum()),
+        "bad_certified": int(bad_cert.sum()),
+        "bad_uncertified": int(bad_uncert.sum()),
+        "ok": bool(bad_cert.sum() == 0 and bad_uncert.sum() == 0),
+    }
+
+
+# ==========================================================================
+# v3.1 int8-residual mode (SquareQ README, "v3.1 - int8-residual mode"): the
+# same format formula with an int8 residual that has one MSE-swept scale per
+# output row, of the rotated residual left by a rank-16 split.  The page
+# names the mode and nothing finer; these readings follow the W4 mode's
+# stated sweep with the int8 grid:
+#
+#  W1 rank 16 (the page's number) through the same svd_init; any rank works.
+#  W2 one scale per row of R (all K values): s_i = fp16(f_i a / 127), a the
+#     row's absmax, f_i = (70 + i)/100 as in the W4 sweep, fp16 as R4.
+#  W3 codes q = clamp(round_half_even(r / s), -128, 127) (the W4 grid's
+#     asymmetric two's-complement range, one byte per code); zero scale -> 0.
+#  W4 the first minimiser of the row's sum of squared errors wins (R6).
+#  W5 codes are stored as int8 [N, K], scales as fp16 [N].
+# ==========================================================================
+W8_QMIN, W8_QMAX = -128, 127
+
+
+def candidate_scale_exact_w8(absmax, i):
+    """Unrounded candidate row scale f_i * absmax / 127 = (70+i)*absmax/12700 (fp64)."""
+    return (70.0 + i) * np.asarray(absmax, np.float64) / 12700.0
+
+
+def codes_for_scale_w8(r, s) -> np.ndarray:
+    """Reading W3: q = clamp(round_half_even(r/s), -128, 127); q = 0 where s == 0."""
+    r = np.asarray(r, np.float64)
+    s = np.asarray(s, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.clip(np.rint(r / s), W8_QMIN, W8_QMAX)
+    return np.where(s == 0, 0.0, q)
+
+
+@dataclass
+class QuantResultW8:
+    q: np.ndarray        # int8 codes [N,K]
+    scale: np.ndarray    # fp16 row scales [N] (float64 holding fp16 values)
+    fidx: np.ndarray     # chosen fraction index [N] (uint8)
+    mse: np.ndarray      # [N,31] sum of squared errors per candidate
+    absmax: np.ndarray   # [N]
+
+
+def quantize_residual_w8(r) -> QuantResultW8:
+    """Sweep the 31 fractions once per row of the rotated residual (W2-W4)."""
+    r = np.asarray(r, np.float64)
+    n, k = r.shape
+    if k % HBLOCK:
+        raise ValueError("K must be a multiple of 256")
+    if not np.all(np.isfinite(r)):
+        raise FloatingPointError("non-finite residual")
+    a = np.abs(r).max(axis=1)
+    mse = np.empty((n, N_FRAC))
+    scales = np.empty((n, N_FRAC))
+    for i in range(N_FRAC):
+        s = fp16_round(candidate_scale_exact_w8(a, i))
+        if np.any(np.isinf(s)):
+            raise FloatingPointError("fp16 scale overflow")
+        q = codes_for_scale_w8(r, s[:, None])
+        mse[:, i] = ((r - q * s[:, None]) ** 2).sum(axis=1)
+        scales[:, i] = s
+    best = np.argmin(mse, axis=1)          # the first minimum
+    s_best = scales[np.arange(n), best]
+    q_best = codes_for_scale_w8(r, s_best[:, None])
+    return QuantResultW8(q_best.astype(np.int8), s_best, best.astype(np.uint8), mse, a)
+
+
+def quantize_weight_w8(w, up, down) -> QuantResultW8:
+    """Builder path of the int8 mode: residual against the bf16 factors, rotation, row sweep."""
+    return quantize_residual_w8(residual(w, up, down))
+
+
+def dequant_w8(q, scale) -> np.ndarray:
+    """D = q * s_row (exact in fp64)."""
+    return np.asarray(q, np.float64) * np.asarray(scale, np.float64)[:, None]
+
+
+def reconstruct_w8(q, scale, up, down) -> np.ndarray:
+    """W_hat = up @ down^T + rotate(dequant_w8(R)) in fp64 (format formula)."""
+    lr = np.asarray(up, np.float64) @ np.asarray(down, np.float64).T
+    return lr + rotate(dequant_w8(q, scale))
+
+
+def forward_w8(x, q, scale, up, down) -> np.ndarray:
+    """y = x @ W_hat^T = rotate(x) @ D^T + (x @ down) @ up^T in fp64."""
+    x = np.asarray(x, np.float64)
+    d = dequant_w8(q, scale)
+    return rotate(x) @ d.T + (x @ np.asarray(down, np.float64)) @ np.asarray(up, np.float64).T
+
+
+def forward_w8_fp16_operands(x, q, scale, up, down) -> np.ndarray:
+    """Diagnostic forward: the activations rounded to fp16 as in
+    forward_fp16_operands (row power of two 2^(11-E)); the codes are exact
+    in fp16 and the row scale is applied to the exact product afterwards;
+    the low-rank term is exact."""
+    x = np.asarray(x, np.float64)
+    xh = rotate(x)
+    amax = np.abs(x).max(axis=1)
+    e = np.zeros(x.shape[0])
+    nz = amax > 0
+    mant, ex = np.frexp(amax[nz])
+    e[nz] = np.where(mant == 0.5, ex - 1, ex)
+    f = np.ldexp(1.0, (11 - e).astype(np.int64))
+    xh16 = fp16_round(xh * f[:, None])
+    y = (xh16 @ np.asarray(q, np.float64).T) * np.asarray(scale, np.float64)[None, :] / f[:, None]
+    return y + (x @ np.asarray(down, np.float64)) @ np.asarray(up, np.float64).T
+
+
+def _variant_mse_w8(r, a):
+    """Row errors of every candidate under each admissible fp16 rounding of
+    its scale (variant 1 differs from variant 0 only within SCALE_MARGIN of
+    a rounding boundary), as in _variant_mse."""
+    n = r.shape[0]
+    sc = np.empty((n, N_FRAC, 2))
+    ms = np.empty((n, N_FRAC, 2))
+    for i in range(N_FRAC):
+        v = candidate_scale_exact_w8(a, i)
+        s0 = fp16_round(v)
+        lo, hi = _fp16_bracket(v)
+        amb = _fp16_boundary_margin(v) <= SCALE_MARGIN
+        s1 = np.where(amb, np.where(s0 == lo, hi, lo), s0)
+        for j, sv in enumerate((s0, s1)):
+            q = codes_for_scale_w8(r, sv[:, None])
+            sc[:, i, j] = sv
+            ms[:, i, j] = ((r - q * sv[:, None]) ** 2).sum(axis=1)
+    return sc, ms
+
+
+def certify_w8(r, res: QuantResultW8):
+    """(rows, near): rows[n] is True where the row's scale choice is far from
+    every tie (the chosen unrounded scale at least SCALE_MARGIN from an fp16
+    rounding boundary and every other candidate's error above the best by
+    SWEEP_MARGIN, under either admissible rounding); near[n, k] flags the
+    values within CODE_MARGIN of a half-integer at the chosen scale, whose
+    code a device residual that differs by fp32 rounding may take either
+    way.  A row holds thousands of values, so codes are certified one by one
+    rather than the whole row at once."""
+    r = np.asarray(r, np.float64)
+    a = res.absmax
+    best = res.fidx.astype(np.int64)
+    ok = _fp16_boundary_margin(candidate_scale_exact_w8(a, best)) > SCALE_MARGIN
+    _, ms = _variant_mse_w8(r, a)
+    others = ms.min(axis=-1)
+    others[np.arange(len(best)), best] = np.inf
+    mse_best = res.mse[np.arange(len(best)), best]
+    ok &= others.min(axis=1) > mse_best * (1 + SWEEP_MARGIN)
+    ok |= (a == 0)
+    s = res.scale[:, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(s > 0, r / np.where(s > 0, s, 1), 0.0)
+    near = (np.abs(t - np.floor(t) - 0.5) < CODE_MARGIN) & (t > W8_QMIN - 1) & (t < W8_QMAX + 1)
+    return ok, near
+
+
+def check_device_quant_w8(r, res: QuantResultW8, q_dev, scale_dev, fidx_dev):
+    """Compare a device int8-mode quantization with the oracle.
+
+    Certified rows must have the oracle's index and scale bit for bit and its
+    codes except at near-tie values (either neighbour).  Other rows must be
+    admissible: the scale an admissible fp16 rounding for the device's index,
+    the codes the requantization with that scale (near-ties either way), and
+    the error within SWEEP_MARGIN of every other candidate's under its least
+    favourable rounding.
+    """
+    r = np.asarray(r, np.float64)
+    n, k = r.shape
+    rows, near_o = certify_w8(r, res)
+    qd = np.asarray(q_dev).astype(np.int64).reshape(n, k)
+    qo = res.q.astype(np.int64)
+    sd = np.asarray(scale_dev, np.float64).reshape(n)
+    fd = np.asarray(fidx_dev).astype(np.int64).reshape(n)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t_o = np.where(res.scale[:, None] > 0, r / np.where(res.scale[:, None] > 0, res.scale[:, None], 1), 0.0)
+    lo_o = np.clip(np.floor(t_o), W8_QMIN, W8_QMAX)
+    hi_o = np.clip(np.ceil(t_o), W8_QMIN, W8_QMAX)
+    codes_same = ((qd == qo) | (near_o & ((qd == lo_o) | (qd == hi_o)))).all(axis=1)
+    same = (fd == res.fidx) & (sd == res.scale) & codes_same
+    bad_cert = rows & ~same
+    sc, ms = _variant_mse_w8(r, res.absmax)
+    fdc = np.clip(fd, 0, N_FRAC - 1)
+    cand = sc[np.arange(n), fdc]
+    scale_ok = (sd == cand[:, 0]) | (sd == cand[:, 1])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(sd[:, None] > 0, r / np.where(sd[:, None] > 0, sd[:, None], 1), 0.0)
+    q_req = np.clip(np.rint(t), W8_QMIN, W8_QMAX)
+    near = np.abs(t - np.floor(t) - 0.5) < CODE_MARGIN
+    q_lo = np.clip(np.floor(t), W8_QMIN, W8_QMAX)
+    q_hi = np.clip(np.ceil(t), W8_QMIN, W8_QMAX)
+    codes_ok = ((qd == q_req) | (near & ((qd == q_lo) | (qd == q_hi)))).all(axis=1)
+    mse_dev = ((r - qd * sd[:, None]) ** 2).sum(axis=1)
+    worst = ms.max(axis=-1)
+    worst[np.arange(n), fdc] = np.inf
+    err_ok = mse_dev <= worst.min(axis=1) * (1 + SWEEP_MARGIN)
+    err_ok |= (res.absmax == 0) & (mse_dev == 0)
+    admissible = scale_ok & codes_ok & err_ok & (fd >= 0) & (fd < N_FRAC)
+    bad_uncert = ~rows & ~same & ~admissible
+    return {
+        "rows": int(n),
+        "uncertified": int((~rows).sum()),
+        "differ": int((~same).sum()),
+        "near_values": int(near_o.sum()),
         "bad_certified": int(bad_cert.sum()),
         "bad_uncertified": int(bad_uncert.sum()),
         "ok": bool(bad_cert.sum() == 0 and bad_uncert.sum() == 0),

@@ -399,6 +399,120 @@ def pin_certification():
         assert O.check_device_quant(r, res, 32, qd, sd, res.fidx)["ok"] == want_ok
 
 
+# ----------------------------------------------------------------- int8-residual mode
+def _sweep_exact_w8(r):
+    """Brute-force row sweep of the int8 mode in exact rational arithmetic."""
+    rf = [Fraction(x) for x in r]
+    a = max(abs(x) for x in rf)
+    best = None
+    for i in range(31):
+        s = _fp16_round_exact(Fraction(70 + i, 12700) * a)
+        q = [0 if s == 0 else min(127, max(-128, _rint_half_even(x / s))) for x in rf]
+        e = sum((x - qq * s) ** 2 for x, qq in zip(rf, q))
+        if best is None or e < best[0]:
+            best = (e, i, s, q)
+    return best
+
+
+def pin_w8_sweep_exact_rational():
+    rng = np.random.default_rng(21)
+    rows = []
+    for _ in range(6):
+        rows.append(rng.integers(-60000, 60001, 256) * 2.0 ** -20)        # dyadic, exact in fp64
+    r = rng.integers(-3000, 3001, 256) * 2.0 ** -16
+    r[7] = -9000 * 2.0 ** -16                                             # absmax on the -128 side
+    rows.append(r)
+    rows.append(np.round(rng.standard_t(2, 256) * 512) * 2.0 ** -12)      # heavy tails
+    # exact half-integer ties at the winning scale (f = 1.00, s = 127 * 2^-12)
+    for _ in range(3):
+        kk = rng.integers(-127, 128, 256).astype(float)
+        kk[0] = 127
+        kk[1:4] = rng.choice([-100.5, -0.5, 0.5, 2.5, 63.5], 3)
+        rows.append(kk * 127 * 2.0 ** -12 / 127)
+    for r in rows:
+        res = O.quantize_residual_w8(r[None, :])
+        e, i, s, q = _sweep_exact_w8(r)
+        assert res.fidx[0] == i
+        assert res.scale[0] == float(s)
+        assert np.array_equal(res.q[0], np.array(q))
+        assert abs(res.mse[0, i] - float(e)) <= 1e-12 * max(float(e), 1e-30)
+
+
+def pin_w8_grid_planted():
+    rng = np.random.default_rng(22)
+    n, k = 6, 768
+    q = rng.integers(-127, 128, (n, k))
+    q[:, 5] = 127 * rng.choice([-1, 1], n)                                # |q| = 127 in every row
+    s = O.fp16_round(rng.uniform(1e-4, 3e-3, n))
+    res = O.quantize_residual_w8(q * s[:, None])
+    assert np.array_equal(res.q, q) and np.array_equal(res.scale, s)
+    assert np.all(res.fidx == 30) and np.all(res.mse[np.arange(n), 30] == 0)
+
+
+def pin_w8_invariances():
+    rng = np.random.default_rng(23)
+    r = rng.standard_normal((5, 512)) * 0.02
+    base = O.quantize_residual_w8(r)
+    for k in (-2, 5):
+        sc = O.quantize_residual_w8(r * 2.0 ** k)
+        assert np.array_equal(sc.q, base.q) and np.array_equal(sc.fidx, base.fidx)
+        assert np.array_equal(sc.scale, base.scale * 2.0 ** k)
+    # a per-row scale: permuting values within a row permutes the codes only
+    perm = rng.permutation(512)
+    pr = O.quantize_residual_w8(r[:, perm])
+    assert np.array_equal(pr.q, base.q[:, perm]) and np.array_equal(pr.fidx, base.fidx)
+    # the chosen error never exceeds plain round-to-nearest at f = 1.00
+    assert np.all(base.mse[np.arange(5), base.fidx] <= base.mse[:, 30])
+    # an all-zero row: scale 0, codes 0, index 0; -128 is reachable
+    z = r.copy(); z[3] = 0
+    zr = O.quantize_residual_w8(z)
+    assert zr.fidx[3] == 0 and zr.scale[3] == 0 and np.all(zr.q[3] == 0)
+    neg = np.linspace(-1.0, 0.4, 256)[None, :]
+    assert O.quantize_residual_w8(neg).q.min() == -128
+    assert base.q.min() >= -128 and base.q.max() <= 127
+
+
+def pin_w8_layer():
+    rng = np.random.default_rng(24)
+    n, k, rank = 48, 512, 16
+    w = rng.standard_normal((n, k)) / np.sqrt(k)
+    up, dn = O.svd_init(w, rank)
+    res = O.quantize_weight_w8(w, up, dn)
+    w_hat = O.reconstruct_w8(res.q, res.scale, up, dn)
+    # the weight round-trips within the int8 grid's error (a step of about
+    # 3.3 sigma / 127 per row), well inside the W4 mode's
+    assert O.rel_fro(w_hat, w) < 1e-2
+    w4 = O.quantize_weight(w, *O.svd_init(w, 32), 32)
+    assert O.rel_fro(w_hat, w) < O.rel_fro(O.reconstruct(w4.q, w4.scale, *O.svd_init(w, 32), 32), w)
+    x = rng.standard_normal((7, k))
+    y = O.forward_w8(x, res.q, res.scale, up, dn)
+    assert np.allclose(y, x @ w_hat.T, rtol=1e-12, atol=1e-12)            # y = x W_hat^T
+    d = O.forward_w8_fp16_operands(x, res.q, res.scale, up, dn)
+    assert O.rel_fro(d, y) < 1e-3
+    # rank 0: the residual is the rotated weight itself
+    r0 = O.quantize_weight_w8(w, np.zeros((n, 0)), np.zeros((k, 0)))
+    assert np.array_equal(r0.q, O.quantize_residual_w8(O.rotate(w)).q)
+
+
+def pin_w8_certification():
+    rng = np.random.default_rng(25)
+    r = rng.standard_normal((40, 768)) * 0.01
+    res = O.quantize_residual_w8(r)
+    rep = O.check_device_quant_w8(r, res, res.q, res.scale, res.fidx)
+    assert rep["ok"] and rep["differ"] == 0
+    rows, near = O.certify_w8(r, res)
+    assert rows.mean() > 0.8
+    i = int(np.argwhere(rows)[0][0])
+    j = int(np.argwhere(~near[i])[0][0])
+    qd = res.q.copy()
+    qd[i, j] = qd[i, j] + 1 if qd[i, j] < 127 else 126                   # one wrong code
+    assert not O.check_device_quant_w8(r, res, qd, res.scale, res.fidx)["ok"]
+    fd = res.fidx.copy(); fd[i] = (fd[i] + 7) % 31                          # a consistent wrong index
+    sd = res.scale.copy(); sd[i] = O.fp16_round(O.candidate_scale_exact_w8(res.absmax[i], fd[i]))
+    qd = res.q.copy(); qd[i] = O.codes_for_scale_w8(r[i], sd[i])
+    assert not O.check_device_quant_w8(r, res, qd, sd, fd)["ok"]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -453,6 +567,19 @@ def _mutations():
     def fraction_off_by_one(a, i):
         return orig_scale(a, np.asarray(i) + 1)
 
+    orig_codes8 = O.sq_oracle.codes_for_scale_w8
+    orig_scale8 = O.sq_oracle.candidate_scale_exact_w8
+
+    def symmetric_clamp_w8(r, s):
+        return np.clip(orig_codes8(r, s), -127, 127)
+
+    def w8_divisor_7(a, i):
+        return orig_scale8(a, i) * 127 / 7
+
+    def w8_scale_per_column(q, scale):
+        q = np.asarray(q, float)
+        return q * np.resize(np.asarray(scale, float), q.shape[1])[None, :]
+
     def svd_no_sqrt(w, rank=32, round_bf16=True):
         w = np.asarray(w, float)
         u, s, vt = np.linalg.svd(w, full_matrices=False)
@@ -470,6 +597,9 @@ def _mutations():
         ("pack", swapped_nibbles),
         ("candidate_scale_exact", fraction_off_by_one),
         ("svd_init", svd_no_sqrt),
+        ("codes_for_scale_w8", symmetric_clamp_w8),
+        ("candidate_scale_exact_w8", w8_divisor_7),
+        ("dequant_w8", w8_scale_per_column),
     ]
 
 
