@@ -43,7 +43,7 @@ typedef enum {
   SQ_E_SHAPE = 2,     /* K % 256 != 0, K < 256, N < 1 or M < 0; the input         */
                       /* gradient also needs N % 64 == 0                          */
   SQ_E_GROUP = 3,     /* group is not 32 or 64                                    */
-  SQ_E_RANK = 4,      /* rank is not 0, 32 or 64                                  */
+  SQ_E_RANK = 4,      /* rank is not 0, 32 or 64 (the int8 mode also takes 16)    */
   SQ_E_ALIGN = 5,     /* a pointer is not 16-byte aligned                         */
   SQ_E_WORKSPACE = 6, /* workspace smaller than the matching *_workspace_bytes()  */
   SQ_E_DTYPE = 7,     /* output dtype is not SQ_F32 or SQ_BF16                    */
@@ -56,7 +56,8 @@ typedef enum { SQ_F32 = 0, SQ_BF16 = 1 } sq_dtype_t;
 /* Bits OR-ed into *dev_flags by the quantizer (read them after a sync). */
 enum {
   SQ_FLAG_NONFINITE = 1,      /* a weight value, or the residual, is NaN or +-inf      */
-  SQ_FLAG_SCALE_OVERFLOW = 2  /* absmax/7 of some group overflows fp16                 */
+  SQ_FLAG_SCALE_OVERFLOW = 2  /* absmax/7 of some group (int8 mode: absmax/127 of some */
+                              /* row) overflows fp16                                   */
 };
 
 /* The W4 payload of one linear layer with N output and K input features.
@@ -148,6 +149,61 @@ size_t sq_linear_dgrad_workspace_bytes(int64_t m, const sq_w4_t *p);
 sq_status_t sq_linear_dgrad(const uint16_t *dy, int64_t m, const sq_w4_t *p, void *dx,
                             sq_dtype_t dx_dtype, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/* ------------------------------------------------------------------------
+ * int8-residual mode (SquareQ README, section "v3.1 - int8-residual mode": the
+ * same format formula with an int8 residual left by a rank-16 split).  The
+ * page names the mode without its details; this library reads it as the W4
+ * sweep on the int8 grid with one scale per output row:
+ *   W_hat = lora_up @ lora_down^T + dequant(R) @ H,  dequant(R)[n][k] = q[n][k] * s[n]
+ * The payload of one layer:
+ *   codes     int8   [n][k]     q in [-128, 127], coordinates after the rotation
+ *   scales    fp16   [n]        one scale per output row (IEEE binary16 bits)
+ *   lora_up   bf16   [n][rank]  rank 0, 16, 32 or 64 (16 is the page's)
+ *   lora_down bf16   [k][rank]
+ * `reserved` must be 0.  Shapes, alignment, streams and errors follow the W4
+ * conventions above. */
+typedef struct {
+  int64_t n, k;
+  int32_t rank, reserved;
+  int8_t *codes;
+  uint16_t *scales;
+  uint16_t *lora_up;
+  uint16_t *lora_down;
+} sq_w8_t;
+
+/* Builder side of the int8 mode: quantize the fp32 weight w [n][k].
+ *   E = w - lora_up @ lora_down^T ;  R = E @ H
+ *   per row with absmax a and for i = 0..30: s_i = fp16(round((70+i)/100 * a / 127)),
+ *   q = clamp(round_half_even(r / s_i), -128, 127) (q = 0 when s_i == 0),
+ *   err_i = sum over the row of (r - q s_i)^2; the first i with the least err wins.
+ * Writes p->codes, p->scales and, when fidx != NULL, fidx[n] = i (uint8).
+ * `workspace` (device, caller-owned, at least
+ * sq_quantize_weight_w8_workspace_bytes(p) bytes) holds the rotated residual
+ * in fp32 between the rotation and the sweep.  dev_flags as for
+ * sq_quantize_weight. */
+size_t sq_quantize_weight_w8_workspace_bytes(const sq_w8_t *p);
+sq_status_t sq_quantize_weight_w8(const float *w, const sq_w8_t *p, uint8_t *fidx,
+                                  int32_t *dev_flags, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/* Rebuild the dense bf16 weight of an int8-mode payload:
+ *   w_hat[n][k] = bf16_round_nearest_even( lora_up @ lora_down^T + (q * s[n]) @ H )
+ * with the rotation summed exactly on integers, one fp32 rounding for the
+ * scale, the rank-r term added in fp32 and one rounding at the end. */
+sq_status_t sq_reconstruct_bf16_w8(const sq_w8_t *p, uint16_t *w_hat, void *stream);
+
+/* Forward of an int8-mode payload:
+ *   y[m][n] = s[n] * sum_k (x @ H)[m][k] q[n][k] + sum_r (x @ lora_down)[m][r] lora_up[n][r]
+ * x bf16 [m][k], y fp32 or bf16 [m][n].  The contraction runs on fp16 MFMA
+ * with the activations treated as in sq_linear_fwd (a power of two per row,
+ * rounded to fp16) and the codes exact in fp16; the row scale multiplies the
+ * fp32 sum.  `workspace` is caller-owned device scratch of at least
+ * sq_linear_fwd_w8_workspace_bytes(m, p) bytes; m == 0 is a no-op. */
+size_t sq_linear_fwd_w8_workspace_bytes(int64_t m, const sq_w8_t *p);
+sq_status_t sq_linear_fwd_w8(const uint16_t *x, int64_t m, const sq_w8_t *p, void *y,
+                             sq_dtype_t y_dtype, void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /* Static description of a status code; never NULL. */
 const char *sq_status_str(sq_status_t status);

@@ -110,3 +110,16 @@ def gen_payload(rng: np.random.Generator, N: int, K: int, group: int, rank: int)
     up = f32_to_bf16_bits((rng.standard_normal((N, rank)) * (1.5 / np.sqrt(N))).astype(np.float32))
     down = f32_to_bf16_bits((rng.standard_normal((K, rank)) * (1.5 / np.sqrt(K))).astype(np.float32))
     return codes, scales, up, down
+
+
+def gen_payload_w8(rng: np.random.Generator, N: int, K: int, rank: int):
+    """A random int8-residual payload with the statistics of a quantized
+    N(0,1/K) weight: int8 codes [N,K] from a clipped rounded normal of
+    spread 30, fp16 row scales around 4.5/sqrt(K)/127, bf16 bits of up
+    [N,rank] and down [K,rank]."""
+    q = np.clip(np.rint(rng.standard_normal((N, K)) * 30.0), -128, 127).astype(np.int8)
+    base = 4.5 / np.sqrt(K) / 127.0
+    scales = (base * np.exp(0.1 * rng.standard_normal(N))).astype(np.float16)
+    up = f32_to_bf16_bits((rng.standard_normal((N, rank)) * (1.5 / np.sqrt(N))).astype(np.float32))
+    down = f32_to_bf16_bits((rng.standard_normal((K, rank)) * (1.5 / np.sqrt(K))).astype(np.float32))
+    return q, scales, up, down

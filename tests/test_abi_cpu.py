@@ -102,3 +102,50 @@ def test_workspace_size_grows_with_m():
     assert sizes[0] > 0 and sizes[0] <= sizes[1] <= sizes[2]
     assert sizes[2] >= 1536 * 3072 * 2                 # holds the rotated activations
     assert _lib.sq_linear_fwd_workspace_bytes(0, p) == 0
+
+
+# ------------------------------------------------------------------ int8-residual mode
+def _payload_w8(n=16, k=256, rank=16, reserved=0, codes=0x1000, scales=0x2000, up=0x3000,
+                down=0x4000):
+    return _lib.SqW8(n, k, rank, reserved, codes, scales, up, down)
+
+
+BAD_W8 = [
+    ("k not multiple of 256", dict(k=300), 2),
+    ("n < 1", dict(n=0), 2),
+    ("rank 8", dict(rank=8), 4),
+    ("reserved set", dict(reserved=1), 4),
+    ("null codes", dict(codes=None), 1),
+    ("null scales", dict(scales=None), 1),
+    ("null down with rank", dict(down=None), 1),
+    ("misaligned codes", dict(codes=0x1004), 5),
+]
+
+
+@pytest.mark.parametrize("why,kw,status", BAD_W8, ids=[b[0] for b in BAD_W8])
+def test_w8_validation_before_launch(why, kw, status):
+    p = _payload_w8(**kw)
+    big = 1 << 40
+    assert _lib.sq_reconstruct_bf16_w8(p, 0x5000, None) == status
+    assert _lib.sq_quantize_weight_w8(0x6000, p, None, 0x7000, 0xB000, big, None) == status
+    assert _lib.sq_linear_fwd_w8(0x8000, 4, p, 0x9000, 0, 0xA000, big, None) == status
+
+
+def test_w8_other_arguments():
+    p = _payload_w8()
+    big = 1 << 40
+    for rank in (0, 16, 32, 64):
+        pr = _payload_w8(rank=rank, up=None if rank == 0 else 0x3000,
+                         down=None if rank == 0 else 0x4000)
+        assert _lib.sq_linear_fwd_w8_workspace_bytes(4, pr) > 0
+    qws = _lib.sq_quantize_weight_w8_workspace_bytes(p)
+    assert qws >= 16 * 256 * 4                        # holds the fp32 rotated residual
+    assert _lib.sq_quantize_weight_w8(0x6000, p, None, 0x7000, 0xB000, qws - 1, None) == 6
+    assert _lib.sq_quantize_weight_w8(0x6000, p, None, 0x7000, None, qws, None) == 1
+    assert _lib.sq_quantize_weight_w8(0x6000, p, 0x7008, 0x7000, 0xB000, qws, None) == 5
+    assert _lib.sq_linear_fwd_w8(0x8000, 0, p, 0x9000, 0, None, 0, None) == 0   # m == 0: no-op
+    assert _lib.sq_linear_fwd_w8(0x8000, -1, p, 0x9000, 0, 0xA000, big, None) == 2
+    assert _lib.sq_linear_fwd_w8(0x8000, 4, p, 0x9000, 7, 0xA000, big, None) == 7
+    ws = _lib.sq_linear_fwd_w8_workspace_bytes(4, p)
+    assert _lib.sq_linear_fwd_w8(0x8000, 4, p, 0x9000, 0, 0xA000, ws - 1, None) == 6
+    assert _lib.sq_reconstruct_bf16_w8(p, None, None) == 1

@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "SQ_OK", 1: "SQ_E_NULL", 2: "SQ_E_SHAPE", 3: "SQ_E_GROUP", 4:
 EXPORTS = ("sq_quantize_weight", "sq_linear_fwd_workspace_bytes", "sq_linear_fwd",
            "sq_linear_fwd_rotate", "sq_linear_fwd_contract", "sq_reconstruct_bf16",
            "sq_linear_dgrad_workspace_bytes", "sq_linear_dgrad", "sq_status_str",
-           "sq_abi_version")
+           "sq_abi_version", "sq_quantize_weight_w8_workspace_bytes", "sq_quantize_weight_w8",
+           "sq_reconstruct_bf16_w8", "sq_linear_fwd_w8_workspace_bytes", "sq_linear_fwd_w8")
 
 
 class SqW4(ctypes.Structure):
@@ -32,6 +33,20 @@ class SqW4(ctypes.Structure):
         ("k", ctypes.c_int64),
         ("group", ctypes.c_int32),
         ("rank", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("lora_up", ctypes.c_void_p),
+        ("lora_down", ctypes.c_void_p),
+    ]
+
+
+class SqW8(ctypes.Structure):
+    """Mirror of sq_w8_t (int8-residual mode)."""
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("rank", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("codes", ctypes.c_void_p),
         ("scales", ctypes.c_void_p),
         ("lora_up", ctypes.c_void_p),
@@ -75,6 +90,17 @@ def lib() -> ctypes.CDLL:
         L.sq_linear_dgrad.restype = ctypes.c_int
         L.sq_reconstruct_bf16.argtypes = [ctypes.POINTER(SqW4), vp, vp]
         L.sq_reconstruct_bf16.restype = ctypes.c_int
+        P8 = ctypes.POINTER(SqW8)
+        L.sq_quantize_weight_w8_workspace_bytes.argtypes = [P8]
+        L.sq_quantize_weight_w8_workspace_bytes.restype = ctypes.c_size_t
+        L.sq_quantize_weight_w8.argtypes = [vp, P8, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sq_quantize_weight_w8.restype = ctypes.c_int
+        L.sq_reconstruct_bf16_w8.argtypes = [P8, vp, vp]
+        L.sq_reconstruct_bf16_w8.restype = ctypes.c_int
+        L.sq_linear_fwd_w8_workspace_bytes.argtypes = [i64, P8]
+        L.sq_linear_fwd_w8_workspace_bytes.restype = ctypes.c_size_t
+        L.sq_linear_fwd_w8.argtypes = [vp, i64, P8, vp, ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.sq_linear_fwd_w8.restype = ctypes.c_int
         L.sq_status_str.argtypes = [ctypes.c_int]
         L.sq_status_str.restype = ctypes.c_char_p
         L.sq_abi_version.argtypes = []
@@ -127,3 +153,27 @@ def sq_linear_dgrad(dy, m: int, p: SqW4, dx, dx_dtype: int, workspace, workspace
                     stream) -> int:
     return lib().sq_linear_dgrad(dy, m, ctypes.byref(p), dx, dx_dtype, workspace,
                                  workspace_bytes, stream)
+
+
+def sq_quantize_weight_w8_workspace_bytes(p: SqW8) -> int:
+    return lib().sq_quantize_weight_w8_workspace_bytes(ctypes.byref(p))
+
+
+def sq_quantize_weight_w8(w, p: SqW8, fidx, dev_flags, workspace, workspace_bytes: int,
+                          stream) -> int:
+    return lib().sq_quantize_weight_w8(w, ctypes.byref(p), fidx, dev_flags, workspace,
+                                       workspace_bytes, stream)
+
+
+def sq_reconstruct_bf16_w8(p: SqW8, w_hat, stream) -> int:
+    return lib().sq_reconstruct_bf16_w8(ctypes.byref(p), w_hat, stream)
+
+
+def sq_linear_fwd_w8_workspace_bytes(m: int, p: SqW8) -> int:
+    return lib().sq_linear_fwd_w8_workspace_bytes(m, ctypes.byref(p))
+
+
+def sq_linear_fwd_w8(x, m: int, p: SqW8, y, y_dtype: int, workspace, workspace_bytes: int,
+                     stream) -> int:
+    return lib().sq_linear_fwd_w8(x, m, ctypes.byref(p), y, y_dtype, workspace, workspace_bytes,
+                                  stream)

@@ -11,7 +11,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import SqError, SqW4, SQ_BF16, SQ_F32
+from ._lib import SqError, SqW4, SqW8, SQ_BF16, SQ_F32
 
 
 @dataclass
@@ -160,4 +160,95 @@ def reconstruct_bf16(p: W4Payload, out: torch.Tensor | None = None):
         out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device=p.codes.device)
     _require(out, torch.bfloat16, "out")
     _check(_lib.sq_reconstruct_bf16(p.abi(), out.data_ptr(), _stream()), "sq_reconstruct_bf16")
+    return out
+
+
+# ---------------------------------------------------------------- int8-residual mode
+@dataclass
+class W8Payload:
+    """Device tensors of one int8-residual layer (layouts as in sq.h)."""
+    codes: torch.Tensor      # int8 [N, K]
+    scales: torch.Tensor     # float16 [N]
+    up: torch.Tensor | None  # bfloat16 [N, rank]
+    down: torch.Tensor | None  # bfloat16 [K, rank]
+
+    @property
+    def n(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.codes.shape[1]
+
+    @property
+    def rank(self) -> int:
+        return 0 if self.up is None else self.up.shape[1]
+
+    def abi(self) -> SqW8:
+        _require(self.codes, torch.int8, "codes")
+        _require(self.scales, torch.float16, "scales")
+        if self.up is not None:
+            _require(self.up, torch.bfloat16, "up")
+            _require(self.down, torch.bfloat16, "down")
+        return SqW8(self.n, self.k, self.rank, 0, _ptr(self.codes), _ptr(self.scales),
+                    _ptr(self.up), _ptr(self.down))
+
+
+def empty_payload_w8(n: int, k: int, rank: int, device="cuda") -> W8Payload:
+    up = torch.empty((n, rank), dtype=torch.bfloat16, device=device) if rank else None
+    down = torch.empty((k, rank), dtype=torch.bfloat16, device=device) if rank else None
+    return W8Payload(torch.empty((n, k), dtype=torch.int8, device=device),
+                     torch.empty((n,), dtype=torch.float16, device=device), up, down)
+
+
+def quantize_weight_w8(w: torch.Tensor, up: torch.Tensor | None, down: torch.Tensor | None,
+                       want_fidx: bool = True, workspace: torch.Tensor | None = None):
+    """sq_quantize_weight_w8: fp32 W [N,K] and bf16 factors -> (payload, fidx, flags tensor)."""
+    _require(w, torch.float32, "w")
+    n, k = w.shape
+    rank = 0 if up is None else up.shape[1]
+    p = empty_payload_w8(n, k, rank, w.device)
+    p.up, p.down = up, down
+    fidx = torch.empty((n,), dtype=torch.uint8, device=w.device) if want_fidx else None
+    flags = torch.zeros(4, dtype=torch.int32, device=w.device)
+    nbytes = _lib.sq_quantize_weight_w8_workspace_bytes(p.abi())
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=w.device)
+    _check(_lib.sq_quantize_weight_w8(w.data_ptr(), p.abi(), _ptr(fidx), flags.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(), _stream()),
+           "sq_quantize_weight_w8")
+    return p, fidx, flags
+
+
+def reconstruct_bf16_w8(p: W8Payload, out: torch.Tensor | None = None):
+    """sq_reconstruct_bf16_w8: int8-mode payload -> bf16 W_hat [N,K]."""
+    if out is None:
+        out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device=p.codes.device)
+    _require(out, torch.bfloat16, "out")
+    _check(_lib.sq_reconstruct_bf16_w8(p.abi(), out.data_ptr(), _stream()),
+           "sq_reconstruct_bf16_w8")
+    return out
+
+
+def fwd_w8_workspace_bytes(m: int, p: W8Payload) -> int:
+    return _lib.sq_linear_fwd_w8_workspace_bytes(m, p.abi())
+
+
+def linear_fwd_w8(x: torch.Tensor, p: W8Payload, out_dtype=torch.float32,
+                  workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """sq_linear_fwd_w8: bf16 x [M,K] -> y [M,N] (fp32 or bf16) for an int8-mode payload."""
+    _require(x, torch.bfloat16, "x")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, p.n), dtype=out_dtype, device=x.device)
+    _require(out, out.dtype, "out")
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (m, p.n):
+        raise ValueError("out must be fp32 or bf16 of shape [M, N]")
+    dt = SQ_BF16 if out.dtype == torch.bfloat16 else SQ_F32
+    nbytes = fwd_w8_workspace_bytes(m, p)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check(_lib.sq_linear_fwd_w8(x.data_ptr(), m, p.abi(), out.data_ptr(), dt,
+                                 workspace.data_ptr(), workspace.numel(), _stream()),
+           "sq_linear_fwd_w8")
     return out

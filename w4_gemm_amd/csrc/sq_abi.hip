@@ -43,6 +43,18 @@ sq_status_t check_payload(const sq_w4_t* p, bool need_codes) {
   return SQ_OK;
 }
 
+sq_status_t check_payload_w8(const sq_w8_t* p) {
+  if (!p) return SQ_E_NULL;
+  if (p->k < 256 || p->k % 256 != 0 || p->n < 1) return SQ_E_SHAPE;
+  if ((p->rank != 0 && p->rank != 16 && p->rank != 32 && p->rank != 64) || p->reserved != 0)
+    return SQ_E_RANK;
+  if (!p->codes || !p->scales) return SQ_E_NULL;
+  if (p->rank > 0 && (!p->lora_up || !p->lora_down)) return SQ_E_NULL;
+  if (!aligned16(p->codes) || !aligned16(p->scales)) return SQ_E_ALIGN;
+  if (p->rank > 0 && (!aligned16(p->lora_up) || !aligned16(p->lora_down))) return SQ_E_ALIGN;
+  return SQ_OK;
+}
+
 sq_status_t from_hip(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_E_HIP; }
 
 }  // namespace
@@ -58,7 +70,7 @@ const char* sq_status_str(sq_status_t s) {
     case SQ_E_SHAPE:
       return "bad shape: need K % 256 == 0, K >= 256, N >= 1, M >= 0 (input gradient: N % 64 == 0)";
     case SQ_E_GROUP: return "group must be 32 or 64";
-    case SQ_E_RANK: return "rank must be 0, 32 or 64";
+    case SQ_E_RANK: return "rank must be 0, 32 or 64 (int8 mode: 0, 16, 32 or 64; reserved 0)";
     case SQ_E_ALIGN: return "every pointer must be 16-byte aligned";
     case SQ_E_WORKSPACE: return "workspace smaller than the entry point's *_workspace_bytes()";
     case SQ_E_DTYPE: return "output dtype must be SQ_F32 or SQ_BF16";
@@ -190,6 +202,66 @@ sq_status_t sq_reconstruct_bf16(const sq_w4_t* p, uint16_t* w_hat, void* stream)
   return from_hip(sq::launch_reconstruct(p->codes, p->scales, p->lora_up, p->lora_down, w_hat,
                                          p->n, p->k, p->group, p->rank,
                                          static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------- int8-residual mode
+size_t sq_quantize_weight_w8_workspace_bytes(const sq_w8_t* p) {
+  if (!p || p->k < 256 || p->k % 256 || p->n < 1) return 0;
+  return sq::quantize_w8_workspace(p->n, p->k);
+}
+
+sq_status_t sq_quantize_weight_w8(const float* w, const sq_w8_t* p, uint8_t* fidx,
+                                  int32_t* dev_flags, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  sq_status_t st = check_payload_w8(p);
+  if (st != SQ_OK) return st;
+  if (!w || !dev_flags || !workspace) return SQ_E_NULL;
+  if (!aligned16(w) || (fidx && !aligned16(fidx)) || !aligned16(dev_flags) ||
+      !aligned16(workspace))
+    return SQ_E_ALIGN;
+  if (workspace_bytes < sq::quantize_w8_workspace(p->n, p->k)) return SQ_E_WORKSPACE;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_quantize_w8(w, p->lora_up, p->lora_down, p->codes, p->scales, fidx,
+                                         dev_flags, p->n, p->k, p->rank, workspace,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+sq_status_t sq_reconstruct_bf16_w8(const sq_w8_t* p, uint16_t* w_hat, void* stream) {
+  sq_status_t st = check_payload_w8(p);
+  if (st != SQ_OK) return st;
+  if (!w_hat) return SQ_E_NULL;
+  if (!aligned16(w_hat)) return SQ_E_ALIGN;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_reconstruct(reinterpret_cast<const uint8_t*>(p->codes), p->scales,
+                                         p->lora_up, p->lora_down, w_hat, p->n, p->k, 0, p->rank,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t sq_linear_fwd_w8_workspace_bytes(int64_t m, const sq_w8_t* p) {
+  if (!p || m <= 0 || p->k < 256 || p->k % 256 || p->n < 1) return 0;
+  return sq::plan_fwd(m, p->n, p->k, 0, p->rank).total;
+}
+
+sq_status_t sq_linear_fwd_w8(const uint16_t* x, int64_t m, const sq_w8_t* p, void* y,
+                             sq_dtype_t y_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (y_dtype != SQ_F32 && y_dtype != SQ_BF16) return SQ_E_DTYPE;
+  sq_status_t st = check_payload_w8(p);
+  if (st != SQ_OK) return st;
+  if (m < 0) return SQ_E_SHAPE;
+  if (m == 0) return SQ_OK;
+  if (!x || !y || !workspace) return SQ_E_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace)) return SQ_E_ALIGN;
+  // group 0 selects the int8 payload in the forward kernels
+  const sq::FwdPlan plan = sq::plan_fwd(m, p->n, p->k, 0, p->rank);
+  if (workspace_bytes < plan.total) return SQ_E_WORKSPACE;
+  if ((st = check_device()) != SQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = from_hip(sq::launch_fwd_rotate(plan, x, p->lora_down, workspace, s))) != SQ_OK)
+    return st;
+  return from_hip(sq::launch_fwd_contract(plan, reinterpret_cast<const uint8_t*>(p->codes),
+                                          p->scales, p->lora_up, y, y_dtype == SQ_BF16, workspace,
+                                          s));
 }
 
 }  // extern "C"

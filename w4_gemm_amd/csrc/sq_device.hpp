@@ -88,6 +88,23 @@ __device__ __forceinline__ half8 dequant8_f16(uint32_t w, _Float16 s) {
                      __builtin_bit_cast(uint32_t, q2 * s2), __builtin_bit_cast(uint32_t, q3 * s2)});
 }
 
+// 8 int8 codes (w0 holds codes 0..3, w1 codes 4..7, one two's-complement
+// byte each) -> fp16 q in the same K order [0,4,1,5,2,6,3,7].  Pair p takes
+// byte p of each word into the low byte of a half (one byte permute), the
+// xor flips the sign bits and sets the fp16 exponent of 1024 (1024 + q + 128)
+// and one packed subtraction leaves q exactly.  Three ops per two codes.
+__device__ __forceinline__ half8 dequant8_i8(uint32_t w0, uint32_t w1) {
+  const half2_t b1152 = {(_Float16)1152.0f, (_Float16)1152.0f};
+  u32x4 o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    // byte selectors: p and 4 + p pick byte p of w0 and of w1, 0x0C a zero byte
+    const uint32_t t = __builtin_amdgcn_perm(w1, w0, 0x0C000C00u | (uint32_t)p | ((4u + p) << 16));
+    o[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, t ^ 0x64806480u) - b1152);
+  }
+  return __builtin_bit_cast(half8, o);
+}
+
 // ---------------------------------------------------------------------------
 // Tiled contractions (forward and input gradient)
 // ---------------------------------------------------------------------------
@@ -200,7 +217,8 @@ __device__ __forceinline__ void fwht256_wave(float (&v)[64], int lane) {
 // The MFMA's row index rho = 4*(l/16)+i of tile t is mapped to column
 // 64*(rho/4) + 4t + rho%4, so each lane's 64 consecutive columns line up with
 // its registers.  sign = -1 flips the bf16 sign bits of `down` (exact).
-// Rows of `up` at or beyond n_rows read as zero; rank is a multiple of 32.
+// Rows of `up` at or beyond n_rows read as zero; rank is a multiple of 16
+// (ranks past `rank` in the last 32-wide step read as zero).
 __device__ __forceinline__ void lowrank_acc_16x256(float (&v)[64], const uint16_t* __restrict__ up,
                                                    const uint16_t* __restrict__ down, int64_t row0,
                                                    int64_t n_rows, int64_t col0, int rank,
@@ -208,9 +226,10 @@ __device__ __forceinline__ void lowrank_acc_16x256(float (&v)[64], const uint16_
   const int c = lane & 15, g = lane >> 4;
   const uint32_t flip = negate ? 0x80008000u : 0u;
   for (int rr = 0; rr < rank; rr += 32) {
+    const bool rk = rr + 8 * g < rank;   // false only in the upper half of a rank-16 step
     // B operand (k = r, col = output row): lane holds up[row0 + c][rr + 8g .. +8]
     bf16x8 bfrag;
-    if (row0 + c < n_rows) {
+    if (rk && row0 + c < n_rows) {
       bfrag = *reinterpret_cast<const bf16x8*>(up + (row0 + c) * rank + rr + 8 * g);
     } else {
       bfrag = (bf16x8){};
@@ -219,7 +238,8 @@ __device__ __forceinline__ void lowrank_acc_16x256(float (&v)[64], const uint16_
     for (int t = 0; t < 16; ++t) {
       // A operand (row rho = c, k = r): down row of column 64*(c/4) + 4t + c%4
       const int64_t col = col0 + 64 * (c >> 2) + 4 * t + (c & 3);
-      u32x4 raw = *reinterpret_cast<const u32x4*>(down + col * rank + rr + 8 * g);
+      u32x4 raw = rk ? *reinterpret_cast<const u32x4*>(down + col * rank + rr + 8 * g)
+                     : (u32x4){0u, 0u, 0u, 0u};
       raw ^= (u32x4){flip, flip, flip, flip};
       const bf16x8 afrag = __builtin_bit_cast(bf16x8, raw);
       f32x4 acc = {v[4 * t], v[4 * t + 1], v[4 * t + 2], v[4 * t + 3]};

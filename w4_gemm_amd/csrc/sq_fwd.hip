@@ -286,7 +286,16 @@ constexpr int WAIT_VM0 = 0x0F70, WAIT_LGKM0 = 0xC07F;
 // `partial` [splits][m][n] for k_fwd_reduce, and split 0 adds the rank-r
 // branch.  plan_fwd picks BM and the split count.  SPLIT = false compiles
 // the single-split kernel without any of the split bookkeeping.
-template <int GSHIFT, int BM, bool SPLIT>   // log2 of the group size, tile rows, split-K
+//
+// GSHIFT = 0 selects the int8-residual payload (SquareQ README, "v3.1 -
+// int8-residual mode"): one stage of B is 64 bytes per weight row, so a
+// super-stage is two stages (128 K values, the same 128-byte LDS rows) and
+// arrives half a super-stage (128 rows, two loads per wave) per stage; a
+// lane reads one 16-byte chunk per column tile and stage and dequantizes it
+// into the two half-steps' fragments with dequant8_i8.  No scales stream
+// with the codes: the row scale multiplies the fp32 sums before the rank-r
+// branch is added.
+template <int GSHIFT, int BM, bool SPLIT>   // log2 of the group size (0: int8), tile rows, split-K
 __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     const uint16_t* __restrict__ xh, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
@@ -294,6 +303,7 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     const float* __restrict__ rowscale, void* __restrict__ y, float* __restrict__ partial,
     int64_t m, int64_t n, int64_t k, int rank, int y_bf16, int kts) {
   static_assert(BM == 256 || BM == 224 || BM == 128, "tile rows");
+  constexpr bool W8 = GSHIFT == 0;
   constexpr int FN = 4;           // wave tile (BM/2) x 64
   constexpr int FM = BM / 32;     // 16-row MFMA tiles per wave
   constexpr int WROWS = BM / 2;   // rows per wave
@@ -308,8 +318,10 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
   const int z = SPLIT ? (int)blockIdx.y : 0;
   const int64_t kt0 = SPLIT ? (int64_t)z * kts : 0;   // first stage of this split
   const int64_t KT = SPLIT ? (int64_t)kts : k / GBK;
-  const int64_t NSS = KT >> 2;            // kts is a multiple of 4
-  const int64_t half_k = k >> 1, ngroups = k >> GSHIFT;
+  const int64_t NSS = W8 ? KT >> 1 : KT >> 2;   // kts is a multiple of 4
+  const int64_t half_k = k >> 1, ngroups = W8 ? 1 : k >> GSHIFT;
+  const int64_t cpr = W8 ? k : half_k;          // code bytes per weight row
+  constexpr int CPS = W8 ? GBK : GBK / 2;       // code bytes per row and stage
 
   const int fr = lane & 15, g = lane >> 4;
 
@@ -323,8 +335,8 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
       (void*)(xh + m0 * k + kt0 * GBK), (short)0, (int)(a_rows * k * 2 - kt0 * GBK * 2),
       0x00020000);
   const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(codes + n0 * half_k + kt0 * (GBK / 2)), (short)0,
-      (int)(b_rows * half_k - kt0 * (GBK / 2)), 0x00020000);
+      (void*)(codes + n0 * cpr + kt0 * CPS), (short)0, (int)(b_rows * cpr - kt0 * CPS),
+      0x00020000);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(scales + n0 * ngroups + ((kt0 * GBK) >> GSHIFT)), (short)0,
       (int)(b_rows * ngroups * 2 - ((kt0 * GBK) >> GSHIFT) * 2), 0x00020000);
@@ -371,6 +383,17 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) bq_issue(ss, qq, bbuf, sbuf);
   };
+  // int8 codes: half hh (rows 128 hh .. +128, sixteen per wave) of super-stage ss
+  auto bh_issue = [&](int64_t ss, int hh, uint8_t* bbuf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 128 * hh + 16 * wave + 8 * i + (lane >> 3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          c_rsrc, (lds_ptr_t)(bbuf + (128 * hh + 16 * wave + 8 * i) * 128), 16,
+          (uint32_t)min(r, b_last) * (uint32_t)cpr + 16 * ((lane & 7) ^ a_swz(8 * i + (lane >> 3))),
+          (int)(ss * 128), 0, 0);
+    }
+  };
 
   // Fragment addresses: for rows r = (WROWS wm | 64 wn) + fr + 16 i the
   // swizzle equals a_swz(fr) (WROWS and 16 are multiples of 16), so row
@@ -399,6 +422,12 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
       bs[j] = *reinterpret_cast<const _Float16*>(sbase + sl + j * 256);
     }
   };
+  // int8: the lane's 16-byte chunk 4s + g (K offsets 16g .. 16g+15 of stage s)
+  auto read_b8 = [&](u32x4 (&bw)[FN], const uint8_t* bbase, int s) {
+    const uint32_t bl = b_row0 * 128 + 16 * ((4 * s + g) ^ swa);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bw[j] = *reinterpret_cast<const u32x4*>(bbase + bl + j * 2048);
+  };
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -424,15 +453,30 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
   // super-stage 1 of B (the loop issues the rest)
   a_issue(0, big_a0);
   a_issue(min((int64_t)1, KT - 1), big_a1);
-  b_issue(0, big_b0, big_s0);
-  bq_issue(min((int64_t)1, NSS - 1), 0, big_b1, big_s1);
+  if constexpr (W8) {
+    bh_issue(0, 0, big_b0);
+    bh_issue(0, 1, big_b0);
+    bh_issue(min((int64_t)1, NSS - 1), 0, big_b1);
+  } else {
+    b_issue(0, big_b0, big_s0);
+    bq_issue(min((int64_t)1, NSS - 1), 0, big_b1, big_s1);
+  }
   sync();
   half8 af0[FM], af1[FM], bj0[FN], bj1[FN];
   uint32_t bw1[FN];
   _Float16 bsc[FN];
-  {
+  u32x2 bw81[FN];   // int8: the second half-step's two words
+  read_a(af0, big_a0, 0);
+  if constexpr (W8) {
+    u32x4 bw[FN];
+    read_b8(bw, big_b0, 0);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      bj0[j] = dequant8_i8(bw[j][0], bw[j][1]);
+      bw81[j] = (u32x2){bw[j][2], bw[j][3]};
+    }
+  } else {
     u32x2 bw[FN];
-    read_a(af0, big_a0, 0);
     read_b(bw, bsc, big_b0, big_s0, 0);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -454,7 +498,8 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     read_a(af1, acur, 1);
     mfma_step(af0, bj0);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bj1[j] = dequant8_f16(bw1[j], bsc[j]);
+    for (int j = 0; j < FN; ++j)
+      bj1[j] = W8 ? dequant8_i8(bw81[j][0], bw81[j][1]) : dequant8_f16(bw1[j], bsc[j]);
 #pragma unroll
     for (int t = 0; t < FM; ++t) {
       SQ_GROUP(0x008, 1);
@@ -469,26 +514,44 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
     sync();
     {
       const int64_t kn = min(kt + 1, KT - 1);
-      const int64_t ssn = kn >> 2;
-      const int64_t ss = (kt + 5) >> 2;
-      u32x2 bw[FN];
       // refill: A of stage kt+2 into this stage's buffer; quarter (kt+5) % 4 of
       // super-stage (kt+5) / 4 of B (a super-stage ss is complete by the
-      // barrier of stage 4 ss - 1, whose second half-step reads it first)
+      // barrier of stage 4 ss - 1, whose second half-step reads it first);
+      // int8: half (kt+3) % 2 of super-stage (kt+3) / 2 (complete by the
+      // barrier of stage 2 ss - 1)
       a_issue(min(kt + 2, KT - 1), aodd ? big_a1 : big_a0);
-      bq_issue(min(ss, NSS - 1), (int)((kt + 5) & 3), (ss & 1) ? big_b1 : big_b0,
-               (ss & 1) ? big_s1 : big_s0);
-      // half-step 1: MFMAs of (kt, 1); read A and B of stage kt+1; dequantize (kt+1, 0)
-      read_b(bw, bsc, (ssn & 1) ? big_b1 : big_b0, (ssn & 1) ? big_s1 : big_s0, (int)(kn & 3));
-      read_a(af0, aodd ? big_a0 : big_a1, 0);
-      mfma_step(af1, bj1);
+      if constexpr (W8) {
+        const int64_t ssn = kn >> 1;
+        const int64_t ss = (kt + 3) >> 1;
+        u32x4 bw[FN];
+        bh_issue(min(ss, NSS - 1), (int)((kt + 3) & 1), (ss & 1) ? big_b1 : big_b0);
+        // half-step 1: MFMAs of (kt, 1); read A and B of stage kt+1; dequantize (kt+1, 0)
+        read_b8(bw, (ssn & 1) ? big_b1 : big_b0, (int)(kn & 1));
+        read_a(af0, aodd ? big_a0 : big_a1, 0);
+        mfma_step(af1, bj1);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        bj0[j] = dequant8_f16(bw[j][0], bsc[j]);
-        bw1[j] = bw[j][1];
+        for (int j = 0; j < FN; ++j) {
+          bj0[j] = dequant8_i8(bw[j][0], bw[j][1]);
+          bw81[j] = (u32x2){bw[j][2], bw[j][3]};
+        }
+      } else {
+        const int64_t ssn = kn >> 2;
+        const int64_t ss = (kt + 5) >> 2;
+        u32x2 bw[FN];
+        bq_issue(min(ss, NSS - 1), (int)((kt + 5) & 3), (ss & 1) ? big_b1 : big_b0,
+                 (ss & 1) ? big_s1 : big_s0);
+        // half-step 1: MFMAs of (kt, 1); read A and B of stage kt+1; dequantize (kt+1, 0)
+        read_b(bw, bsc, (ssn & 1) ? big_b1 : big_b0, (ssn & 1) ? big_s1 : big_s0, (int)(kn & 3));
+        read_a(af0, aodd ? big_a0 : big_a1, 0);
+        mfma_step(af1, bj1);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          bj0[j] = dequant8_f16(bw[j][0], bsc[j]);
+          bw1[j] = bw[j][1];
+        }
       }
       SQ_GROUP(0x020, 6);
-      SQ_GROUP(0x100, 8);
+      SQ_GROUP(0x100, W8 ? 4 : 8);
 #pragma unroll
       for (int t = 0; t < FM; ++t) {
         SQ_GROUP(0x008, 1);
@@ -508,8 +571,19 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
 #undef SQ_GROUP
 
   const int64_t rbase = m0 + WROWS * wm, cbase = n0 + 64 * wn;
+  if constexpr (W8) {
+    // the row scale of output column c multiplies the code sums
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const float sc = fp16_bits_to_f32(scales[min(cbase + 16 * j + fr, n - 1)]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) acc[i][j] *= sc;
+    }
+  }
   // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA into the same accumulators
+  // (rank 16: the upper half of the 32-wide step reads zeros)
   for (int rr = 0; rr < (z == 0 ? rank : 0); rr += 32) {   // (z is 0 unless SPLIT)
+    const bool rk = rr + 8 * g < rank;
 #pragma unroll
     for (int hl = 0; hl < 2; ++hl) {
       const uint16_t* tsrc = hl ? tlo : thi;
@@ -517,12 +591,13 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int64_t r = min(rbase + 16 * i + fr, m - 1);
-        af[i] = *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + 8 * g);
+        af[i] = rk ? *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + 8 * g) : (bf16x8){};
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int64_t c = min(cbase + 16 * j + fr, n - 1);
-        const bf16x8 bj = *reinterpret_cast<const bf16x8*>(up + c * rank + rr + 8 * g);
+        const bf16x8 bj =
+            rk ? *reinterpret_cast<const bf16x8*>(up + c * rank + rr + 8 * g) : (bf16x8){};
 #pragma unroll
         for (int i = 0; i < FM; ++i)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bj, acc[i][j], 0, 0, 0);
@@ -620,6 +695,11 @@ __global__ void __launch_bounds__(BIG_THREADS, 1) k_fwd_gemm_big(
 // M and weight rows past N come back as zeros from range-checked buffer
 // loads.  Split-K partials go to the workspace (fixed-order sum in
 // k_fwd_reduce); split 0 also adds the rank-r branch.
+//
+// GSHIFT = 0 selects the int8-residual payload: 32 bytes of codes per lane,
+// weight-row tile and chunk (MFMA step e reads bytes 8e .. 8e+7), no group
+// scales, and the row scale applied to the fp32 sums before the rank-r
+// branch is added.
 constexpr int SK_ROWS = 64;
 
 template <int GSHIFT, int MT>
@@ -628,15 +708,18 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
     const uint16_t* __restrict__ scales, const uint16_t* __restrict__ thi,
     const uint16_t* __restrict__ tlo, const uint16_t* __restrict__ up,
     float* __restrict__ partial, int64_t m, int64_t n, int64_t k, int rank, int kslice) {
+  constexpr bool W8 = GSHIFT == 0;
+  constexpr int CW = W8 ? 2 : 1;   // 16-byte code loads per weight-row tile and chunk
   const int lane = threadIdx.x, fr = lane & 15, g = lane >> 4;
   // K slice fastest: neighbouring workgroups sweep whole weight rows
   const int64_t n0 = (int64_t)blockIdx.y * SK_ROWS;
   const int ks = blockIdx.x;
   const int64_t k0 = (int64_t)ks * kslice, k1 = min(k, k0 + kslice);
-  const int64_t half_k = k >> 1, ngroups = k >> GSHIFT;
+  const int64_t ngroups = W8 ? 1 : k >> GSHIFT;
+  const int64_t cpr = W8 ? k : k >> 1;   // code bytes per weight row
   const int64_t b_rows = min((int64_t)SK_ROWS, n - n0);
   const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(codes + n0 * half_k), (short)0, (int)(b_rows * half_k), 0x00020000);
+      (void*)(codes + n0 * cpr), (short)0, (int)(b_rows * cpr), 0x00020000);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(scales + n0 * ngroups), (short)0, (int)(b_rows * ngroups * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -645,7 +728,7 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
   uint32_t c_off[4], s_off[4], a_off[MT];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    c_off[t] = (uint32_t)((16 * t + fr) * half_k) + 16u * g;
+    c_off[t] = (uint32_t)((16 * t + fr) * cpr) + (uint32_t)(16 * CW) * g;
     s_off[t] = (uint32_t)((16 * t + fr) * ngroups) * 2u;
   }
 #pragma unroll
@@ -654,15 +737,23 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
   // kb < 0 asks for nothing: the offsets land past the descriptors' range,
   // so the loads return zeros without touching memory (no branch, so the
   // compiler's wait counting stays exact)
-  auto load_codes = [&](u32x4 (&cw)[4], uint32_t (&sc)[4], int64_t kb) {
+  auto load_codes = [&](u32x4 (&cw)[4 * CW], uint32_t (&sc)[4], int64_t kb) {
     const uint32_t off = kb < 0 ? 0x80000000u : 0u;
     kb = kb < 0 ? 0 : kb;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      cw[t] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off + c_off[t] + (uint32_t)(kb >> 1), 0,
-                                                    0);
-      sc[t] = __builtin_amdgcn_raw_buffer_load_b16(
-          s_rsrc, off + s_off[t] + (uint32_t)(((kb + 32 * g) >> GSHIFT) * 2), 0, 0);
+      if constexpr (W8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          cw[2 * t + h] = __builtin_amdgcn_raw_buffer_load_b128(
+              c_rsrc, off + c_off[t] + (uint32_t)kb + 16u * h, 0, 0);
+        sc[t] = 0;
+      } else {
+        cw[t] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off + c_off[t] + (uint32_t)(kb >> 1),
+                                                      0, 0);
+        sc[t] = __builtin_amdgcn_raw_buffer_load_b16(
+            s_rsrc, off + s_off[t] + (uint32_t)(((kb + 32 * g) >> GSHIFT) * 2), 0, 0);
+      }
     }
   };
 
@@ -675,7 +766,7 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
   // into the registers the previous chunk used (loads complete in order, so
   // waiting for the activations leaves that prefetch in flight); two
   // register sets alternate, so no copy forces an early wait.
-  auto chunk = [&](const u32x4 (&cw)[4], const uint32_t (&sc)[4], u32x4 (&cn)[4],
+  auto chunk = [&](const u32x4 (&cw)[4 * CW], const uint32_t (&sc)[4], u32x4 (&cn)[4 * CW],
                    uint32_t (&sn)[4], int64_t kb, int64_t kpre) {
     half8 af[MT][4];
 #pragma unroll
@@ -690,7 +781,10 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
     for (int t = 0; t < 4; ++t) {
       const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sc[t]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bf[t][e] = dequant8_f16(cw[t][e], sv);
+      for (int e = 0; e < 4; ++e)
+        bf[t][e] = W8 ? dequant8_i8(cw[CW * t + (e >> 1)][2 * (e & 1)],
+                                    cw[CW * t + (e >> 1)][2 * (e & 1) + 1])
+                      : dequant8_f16(cw[CW * t][e], sv);
     }
     load_codes(cn, sn, kpre);
     __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
@@ -703,7 +797,7 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
           acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt][e], bf[t][e], acc[mt][t], 0, 0, 0);
   };
   // the slice is a whole number of 256-value pairs of chunks
-  u32x4 cw0[4], cw1[4];
+  u32x4 cw0[4 * CW], cw1[4 * CW];
   uint32_t sc0[4], sc1[4];
   load_codes(cw0, sc0, k0);
   __builtin_amdgcn_sched_barrier(0);   // chunk 0's codes are issued first
@@ -714,9 +808,20 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
     chunk(cw1, sc1, cw1, sc1, kb + 128, more ? kb + 384 : -1);
   }
 
+  if constexpr (W8) {
+    // the row scale of output column c multiplies the code sums
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float sc = fp16_bits_to_f32(scales[min(n0 + 16 * t + fr, n - 1)]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt][t] *= sc;
+    }
+  }
   if (ks == 0) {
-    // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA
+    // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA (rank 16: the upper
+    // half of the 32-wide step reads zeros)
     for (int rr = 0; rr < rank; rr += 32) {
+      const bool rk = rr + 8 * g < rank;
 #pragma unroll
       for (int hl = 0; hl < 2; ++hl) {
         const uint16_t* tsrc = hl ? tlo : thi;
@@ -724,12 +829,13 @@ __global__ void __launch_bounds__(64) k_fwd_skinny(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int64_t c = min(n0 + 16 * t + fr, n - 1);
-          bu[t] = *reinterpret_cast<const bf16x8*>(up + c * rank + rr + 8 * g);
+          bu[t] = rk ? *reinterpret_cast<const bf16x8*>(up + c * rank + rr + 8 * g) : (bf16x8){};
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int64_t r = min((int64_t)(16 * mt + fr), m - 1);
-          const bf16x8 at = *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + 8 * g);
+          const bf16x8 at =
+              rk ? *reinterpret_cast<const bf16x8*>(tsrc + r * rank + rr + 8 * g) : (bf16x8){};
 #pragma unroll
           for (int t = 0; t < 4; ++t)
             acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(at, bu[t], acc[mt][t], 0, 0, 0);
@@ -797,7 +903,7 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
     // under ~15 % of the payload bytes
     p.skinny_mt = m <= 16 ? 1 : m <= 32 ? 2 : 4;
     const int64_t ntiles = (n + SK_ROWS - 1) / SK_ROWS;
-    const double pay = (double)n * k * (0.5 + 2.0 / group);
+    const double pay = group ? (double)n * k * (0.5 + 2.0 / group) : (double)n * k;
     int64_t s = (1024 + ntiles - 1) / ntiles;
     s = std::min<int64_t>(s, std::max<int64_t>(1, (int64_t)(0.15 * pay / (4.0 * m * n))));
     s = std::max<int64_t>(1, s);
@@ -880,6 +986,9 @@ hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t
   if (p.rank == 0)
     hipLaunchKernelGGL(k_fwd_stats<0>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m, p.k,
                        p.pre_bps, b.amax, b.tpart);
+  else if (p.rank == 16)
+    hipLaunchKernelGGL(k_fwd_stats<16>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m,
+                       p.k, p.pre_bps, b.amax, b.tpart);
   else if (p.rank == 32)
     hipLaunchKernelGGL(k_fwd_stats<32>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m,
                        p.k, p.pre_bps, b.amax, b.tpart);
@@ -905,7 +1014,9 @@ hipError_t launch_fwd_contract(const FwdPlan& p, const uint8_t* codes, const uin
 #define SQ_SKINNY(GS, MT)                                                                         \
   hipLaunchKernelGGL((k_fwd_skinny<GS, MT>), sg, dim3(64), 0, stream, b.xh, codes, scales, b.thi, \
                      b.tlo, up, b.partial, p.m, p.n, p.k, p.rank, p.skinny_kslice)
-    if (p.group == 32) {
+    if (p.group == 0) {
+      if (p.skinny_mt == 1) SQ_SKINNY(0, 1); else if (p.skinny_mt == 2) SQ_SKINNY(0, 2); else SQ_SKINNY(0, 4);
+    } else if (p.group == 32) {
       if (p.skinny_mt == 1) SQ_SKINNY(5, 1); else if (p.skinny_mt == 2) SQ_SKINNY(5, 2); else SQ_SKINNY(5, 4);
     } else {
       if (p.skinny_mt == 1) SQ_SKINNY(6, 1); else if (p.skinny_mt == 2) SQ_SKINNY(6, 2); else SQ_SKINNY(6, 4);
@@ -920,7 +1031,9 @@ hipError_t launch_fwd_contract(const FwdPlan& p, const uint8_t* codes, const uin
 #define SQ_BIG_BM(GS, SP)                                                                       \
   if (p.tile_m == 224) SQ_BIG(GS, 224, SP); else if (p.tile_m == 256) SQ_BIG(GS, 256, SP);     \
   else SQ_BIG(GS, 128, SP)
-    if (p.group == 32) {
+    if (p.group == 0) {
+      if (p.splits > 1) { SQ_BIG_BM(0, true); } else { SQ_BIG_BM(0, false); }
+    } else if (p.group == 32) {
       if (p.splits > 1) { SQ_BIG_BM(5, true); } else { SQ_BIG_BM(5, false); }
     } else {
       if (p.splits > 1) { SQ_BIG_BM(6, true); } else { SQ_BIG_BM(6, false); }

@@ -13,6 +13,15 @@ hipError_t launch_quantize(const float* w, const uint16_t* up, const uint16_t* d
                            uint8_t* codes, uint16_t* scales, uint8_t* fidx, int32_t* flags,
                            int64_t n, int64_t k, int group, int rank, hipStream_t stream);
 
+// int8-residual mode quantizer (two launches around an fp32 copy of the
+// rotated residual in the workspace).  The reconstruct is launch_reconstruct
+// with group 0.
+size_t quantize_w8_workspace(int64_t n, int64_t k);
+hipError_t launch_quantize_w8(const float* w, const uint16_t* up, const uint16_t* down,
+                              int8_t* codes, uint16_t* scales, uint8_t* fidx, int32_t* flags,
+                              int64_t n, int64_t k, int rank, void* workspace,
+                              hipStream_t stream);
+
 // Forward: workspace layout and launch.
 struct FwdPlan {
   int64_t m, n, k;

@@ -16,6 +16,11 @@
 // fp32 sums) and writes its row through an LDS transpose so that every store
 // instruction covers two whole 512-byte row segments.  HBM-bound: reads
 // 0.5 + 2/group bytes and writes 2 bytes per weight element.
+//
+// The same kernel rebuilds the int8-residual mode (SquareQ README, "v3.1 -
+// int8-residual mode"; GROUP = 0 selects it): 64 bytes of codes per lane
+// and strip, one scale per row, the butterflies on exact integers in fp32
+// and the scale applied once after the last stage.
 #include "sq_device.hpp"
 #include "sq_kernels.h"
 
@@ -83,14 +88,34 @@ __device__ __forceinline__ void dequant_rotate64(float (&v)[64], const u32x4 (&w
   }
 }
 
+// int8 codes: the lane's 64 bytes (element e = column 64g + e of the block)
+// rotated over the six in-lane column bits, unscaled:
+// v[e] = sum_e' S64[e][e'] q[e'].  Each byte converts to fp32 as q + 128 (the
+// sign bit flipped) in one instruction; the butterflies run on these exact
+// integers (every partial sum is below 2^14 in magnitude), and because S64
+// sends the constant 128 to column 0 alone (as 64 * 128), one subtraction
+// there removes the offset.
+__device__ __forceinline__ void dequant_rotate64_w8(float (&v)[64], const u32x4 (&w)[4]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t word = w[j >> 2][j & 3] ^ 0x80808080u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) v[4 * j + b] = (float)((word >> (8 * b)) & 0xFFu);
+  }
+  fwht_inreg64(v);
+  v[0] -= 8192.0f;
+}
+
 // LDS staging rows: 256 bf16 = 32 x 16 bytes, padded by one 16-byte slot so
 // that the 16 rows written by one instruction start in different banks.
 constexpr int STAGE_ROW_U4 = 33;
 constexpr int REC_WAVES = 4;
 
-// Payload of one lane for one strip: 32 bytes of codes, two scales / 16.
+// Payload of one lane for one strip: 32 bytes of int4 codes and two scales,
+// or 64 bytes of int8 codes and the row scale.
+template <int GROUP>
 struct StripIn {
-  u32x4 w[2];
+  u32x4 w[GROUP == 0 ? 4 : 2];
   uint32_t s2;   // fp16 bits: low half for columns 0..31 of the chunk, high for 32..63
 };
 
@@ -100,10 +125,17 @@ struct StripIn {
 // the compiler wait for every outstanding memory operation, stores included,
 // before the next strip.
 template <int GROUP>
-__device__ __forceinline__ void load_strip(StripIn& in, const uint8_t* cbase,
+__device__ __forceinline__ void load_strip(StripIn<GROUP>& in, const uint8_t* cbase,
                                            const uint16_t* sbase, int g) {
   // plain loads: on gfx950 the non-temporal load path streams these
   // 32-byte row pieces markedly slower (63.5 vs 49.5 us at 16384x6144)
+  if constexpr (GROUP == 0) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(cbase + 64 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) in.w[i] = src[i];
+    in.s2 = sbase[0];
+    return;
+  }
   const u32x4* src = reinterpret_cast<const u32x4*>(cbase + 32 * g);
   in.w[0] = src[0];
   in.w[1] = src[1];
@@ -136,7 +168,8 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ up, const uint16_t* __restrict__ down,
     uint16_t* __restrict__ w_hat, int64_t n, int64_t k, int strips) {
-  constexpr int RC = RANK / 32;   // rank-32 chunks
+  constexpr bool W8 = GROUP == 0;
+  constexpr int RC = (RANK + 31) / 32;   // rank-32 chunks (rank 16: the upper half reads zero)
   // A operands of the low-rank MFMA for the block, in fragment order
   // [chunk][t][lane] so that every read is 64 consecutive 16-byte slots.
   __shared__ u32x4 s_down[RC > 0 ? RC * 16 * 64 : 1];
@@ -160,16 +193,19 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
     const int f = tid + 64 * REC_WAVES * m;
     const int q = f >> 10, t = (f >> 6) & 15, l = f & 63;
     const int64_t dcol = blk * 256 + swap_col((l & 15) >> 2, 4 * t + (l & 3));
-    s_down[f] = *reinterpret_cast<const u32x4*>(down + dcol * RANK + 32 * q + 8 * (l >> 4));
+    s_down[f] = 32 * q + 8 * (l >> 4) < RANK
+                    ? *reinterpret_cast<const u32x4*>(down + dcol * RANK + 32 * q + 8 * (l >> 4))
+                    : (u32x4){0u, 0u, 0u, 0u};
   }
   __syncthreads();
   if (first >= nstr) return;
 
-  const int64_t spr = k / GROUP;   // scales per row
+  const int64_t spr = W8 ? 1 : k / (GROUP > 0 ? GROUP : 1);   // scales per row
+  const int64_t cpr = W8 ? k : k >> 1;                        // code bytes per row
   // byte offset of the lane's 16-byte store piece from the strip's first row
   const uint32_t stoff = 2u * ((uint32_t)((lane >> 5) * k) + (uint32_t)(blk * 256) + 8u * (lane & 31));
-  const uint8_t* cblk = codes + blk * 128;
-  const uint16_t* sblk = scales + blk * (256 / GROUP);
+  const uint8_t* cblk = codes + blk * (W8 ? 256 : 128);
+  const uint16_t* sblk = scales + (W8 ? 0 : blk * (256 / (GROUP > 0 ? GROUP : 1)));
   u32x4* stage = &s_stage[wave][0];
   // the lane's row of strip st, clamped to the last row
   auto lrow = [&](int64_t st) { return min(st * 16 + c, n - 1); };
@@ -183,12 +219,17 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
   // strip's stores (from LDS) and the next strip's loads back to back, and
   // only then computes: the next wait is a whole strip of compute later.
   const int cnt = (int)min((int64_t)strips, (nstr - first + REC_WAVES - 1) / REC_WAVES);
-  StripIn cur;
+  StripIn<GROUP> cur;
   bf16x8 ufrag[RC > 0 ? RC : 1];
-  load_strip<GROUP>(cur, cblk + lrow(first) * (k >> 1), sblk + lrow(first) * spr, g);
+  auto load_up = [&](bf16x8 (&uf)[RC > 0 ? RC : 1], int64_t row) {
 #pragma unroll
-  for (int q = 0; q < RC; ++q)
-    ufrag[q] = *reinterpret_cast<const bf16x8*>(up + lrow(first) * RANK + 32 * q + 8 * g);
+    for (int q = 0; q < RC; ++q)
+      uf[q] = 32 * q + 8 * g < RANK
+                  ? *reinterpret_cast<const bf16x8*>(up + row * RANK + 32 * q + 8 * g)
+                  : (bf16x8){};
+  };
+  load_strip<GROUP>(cur, cblk + lrow(first) * cpr, sblk + lrow(first) * spr, g);
+  load_up(ufrag, lrow(first));
 
   for (int i = 0; i < cnt; ++i) {
     const int64_t st = first + (int64_t)REC_WAVES * i;
@@ -196,24 +237,30 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
     __builtin_amdgcn_s_waitcnt(SQ_WAIT_VM0);
     __builtin_amdgcn_sched_barrier(0);
     // consume this strip's payload, then reuse its registers
-    const StripIn in = cur;
+    const StripIn<GROUP> in = cur;
     bf16x8 uf[RC > 0 ? RC : 1];
 #pragma unroll
     for (int q = 0; q < RC; ++q) uf[q] = ufrag[q];
     if (i > 0) store_tile(stage, w_hat, row0 - 16 * REC_WAVES, n, k, stoff, lane);
     if (i + 1 < cnt) {
       const int64_t nst = st + REC_WAVES;
-      load_strip<GROUP>(cur, cblk + lrow(nst) * (k >> 1), sblk + lrow(nst) * spr, g);
-#pragma unroll
-      for (int q = 0; q < RC; ++q)
-        ufrag[q] = *reinterpret_cast<const bf16x8*>(up + lrow(nst) * RANK + 32 * q + 8 * g);
+      load_strip<GROUP>(cur, cblk + lrow(nst) * cpr, sblk + lrow(nst) * spr, g);
+      load_up(ufrag, lrow(nst));
     }
     __builtin_amdgcn_sched_barrier(0);
 
     float v[64];
-    dequant_rotate64(v, in.w, fp16_bits_to_f32(in.s2 & 0xFFFFu) * 0.0625f,
-                     fp16_bits_to_f32(in.s2 >> 16) * 0.0625f);
-    fwht_cross64_swap(v);
+    if constexpr (W8) {
+      dequant_rotate64_w8(v, in.w);
+      fwht_cross64_swap(v);   // exact: integers of magnitude at most 2^15
+      const float s16 = fp16_bits_to_f32(in.s2) * 0.0625f;
+#pragma unroll
+      for (int e = 0; e < 64; ++e) v[e] *= s16;
+    } else {
+      dequant_rotate64(v, in.w, fp16_bits_to_f32(in.s2 & 0xFFFFu) * 0.0625f,
+                       fp16_bits_to_f32(in.s2 >> 16) * 0.0625f);
+      fwht_cross64_swap(v);
+    }
 #pragma unroll
     for (int q = 0; q < RC; ++q)
 #pragma unroll
@@ -256,7 +303,10 @@ template <int RANK>
 static void launch_rank(dim3 grid, int group, hipStream_t stream, const uint8_t* codes,
                         const uint16_t* scales, const uint16_t* up, const uint16_t* down,
                         uint16_t* w_hat, int64_t n, int64_t k, int s) {
-  if (group == 32)
+  if (group == 0)
+    hipLaunchKernelGGL((k_reconstruct<RANK, 0>), grid, dim3(64 * REC_WAVES), 0, stream, codes,
+                       scales, up, down, w_hat, n, k, s);
+  else if (group == 32)
     hipLaunchKernelGGL((k_reconstruct<RANK, 32>), grid, dim3(64 * REC_WAVES), 0, stream, codes,
                        scales, up, down, w_hat, n, k, s);
   else
@@ -273,6 +323,8 @@ hipError_t launch_reconstruct(const uint8_t* codes, const uint16_t* scales, cons
   dim3 grid((unsigned)(runs * nblk));
   if (rank == 0)
     launch_rank<0>(grid, group, stream, codes, scales, up, down, w_hat, n, k, s);
+  else if (rank == 16)
+    launch_rank<16>(grid, group, stream, codes, scales, up, down, w_hat, n, k, s);
   else if (rank == 32)
     launch_rank<32>(grid, group, stream, codes, scales, up, down, w_hat, n, k, s);
   else
