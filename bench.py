@@ -25,8 +25,10 @@ host's cores.
 Extra fields: the input gradient (sq_linear_dgrad, dx = dy W_hat, same
 flop count as the forward, not part of the step), the streaming builder's
 wall time on a two-layer fp32 checkpoint, the small-M forward sweep (M = 1, 16, 128 on the
-6144x16384 g32 weight) in GB/s of bytes the call must move, and the
-rotation, reconstruct and quantize kernels against HBM peak.
+6144x16384 g32 weight) in GB/s of bytes the call must move, the
+rotation, reconstruct and quantize kernels against HBM peak, and the
+int8-residual mode (rank 16, one int8 code per weight and one fp16 scale
+per row) at the same shape: its forward, reconstruct and quantizer.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 4]
        python bench.py --ops copy      (the counter calibration copy only)
@@ -87,7 +89,7 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--ops", default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs")
+    ap.add_argument("--ops", default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs,w8")
     ap.add_argument("--small-m", default="1,16,128")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -205,6 +207,9 @@ def main():
             b.record()
         torch.cuda.synchronize()
         res["quantize"] = np.array([a.elapsed_time(b) for a, b in marks])
+    # ---------------------------------------------------------------- int8-residual mode
+    if "w8" in ops:
+        res["w8"] = w8_run(torch, W, dev, w, x, what, M, N, K, args.steps, args.warmup)
     # ---------------------------------------------------------------- streaming builder
     if "builder" in ops:
         res["builder"] = builder_run(torch, dev)
@@ -271,6 +276,8 @@ def main():
         out["dgrad_pct_bf16_mfma_peak"] = 100.0 * out["dgrad_tflops"] / PEAK_F16_TFLOPS
     if "builder" in res:
         out["builder"] = res["builder"]
+    if "w8" in res:
+        out["w8"] = res["w8"]
     if "smallm" in res:
         out["fwd_small_m"] = res["smallm"]
     if "configs" in res:
@@ -303,6 +310,57 @@ def main():
         line["cpu_baseline"] = cpu_baseline(p0, x, cfg, args.cpu_rows)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def w8_run(torch, W, dev, w, x, what, M, N, K, steps, warmup):
+    """The int8-residual mode at the same layer shape with rank-16 factors:
+    sq_quantize_weight_w8 of the same weight, then sq_linear_fwd_w8 (whole
+    call: rotation pre-phase + int8 contraction) and sq_reconstruct_bf16_w8
+    (rotating over three payload/output sets), each timed with HIP events."""
+    R = 16
+    torch.manual_seed(0)
+    u, s, v = torch.svd_lowrank(w, q=R + 8, niter=2)
+    rs = s[:R].sqrt()
+    up = (u[:, :R] * rs).to(torch.bfloat16).contiguous()
+    down = (v[:, :R] * rs).to(torch.bfloat16).contiguous()
+    del u, s, v
+    qws = torch.empty(W._lib.sq_quantize_weight_w8_workspace_bytes(W.empty_payload_w8(N, K, R, dev).abi()),
+                      dtype=torch.uint8, device=dev)
+    p0, fidx, flags = W.quantize_weight_w8(w, up, down, workspace=qws)
+    torch.cuda.synchronize()
+    assert int(flags[0]) == 0, "int8 quantizer flagged the synthetic weight"
+    pays = [p0] + [W.W8Payload(p0.codes.clone(), p0.scales.clone(), up, down) for _ in range(2)]
+    ws = torch.empty(W.fwd_w8_workspace_bytes(M, p0), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        marks = [(ev(), ev()) for _ in range(steps)]
+        for i, (a, b) in enumerate(marks):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in marks]))
+
+    t_fwd = timed(lambda i: W.linear_fwd_w8(x, p0, out=y, workspace=ws))
+    t_rec = timed(lambda i: W.reconstruct_bf16_w8(pays[i % 3], out=what[i % 3]))
+    t_q = timed(lambda i: W.quantize_weight_w8(w, up, down, want_fidx=False, workspace=qws))
+    flops = 2.0 * M * N * K + 2.0 * M * R * (N + K)
+    pay = N * K + 2.0 * N + (N + K) * R * 2
+    rec_bytes = pay + 2.0 * N * K
+    out = {"rank": R, "fwd_ms": t_fwd, "fwd_tflops": flops / (t_fwd * 1e-3) / 1e12,
+           "reconstruct_ms": t_rec, "reconstruct_gbps": rec_bytes / (t_rec * 1e-3) / 1e9,
+           "quantize_ms": t_q}
+    out["fwd_pct_bf16_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_F16_TFLOPS
+    out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
+    del pays, p0, qws, ws, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def copy_calibration(torch, dev, reps=5):
