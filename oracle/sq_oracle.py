@@ -718,3 +718,210 @@ def check_device_quant_w8(r, res: QuantResultW8, q_dev, scale_dev, fidx_dev):
         "bad_uncertified": int(bad_uncert.sum()),
         "ok": bool(bad_cert.sum() == 0 and bad_uncert.sum() == 0),
     }
+
+
+# ==========================================================================
+# 4-bit float mode (the "Residual codecs" bullet's FP4 alternative: e2m1
+# elements with block scales, driving native FP4 matrix instructions; the
+# page's op-level parity line describes the forward as rotate + block-quant of
+# the activations + FP4 product + epilogue).  The page's NVFP4 variant
+# (ue4m3 block-16 scales, per-tensor scale, an NVIDIA tiled layout) exists
+# for one vendor's instructions; the format here is its OCP MX counterpart,
+# MXFP4, which the gfx950 scaled matrix instructions take.  Readings:
+#
+#  X1 element: FP4 E2M1 (1 sign, 2 exponent bits of bias 1, 1 mantissa bit):
+#     magnitudes 0, 0.5 (the subnormal), 1, 1.5, 2, 3, 4, 6; nibble
+#     s<<3 | e<<1 | m.  A value whose magnitude rounds to 0 gets nibble 0.
+#  X2 block: 32 consecutive values along K share one E8M0 scale 2^(e-127).
+#  X3 scale: e = floor(log2(absmax)) - 2 + 127 (2 = the largest E2M1
+#     exponent), clamped to [0, 254]; an all-zero block gets e = 0.
+#  X4 rounding: v / 2^(e-127) to the nearest E2M1 value, ties to the even
+#     mantissa, magnitudes above 6 saturate to 6.
+#  X5 operands: the rotated residual R of the W4 mode (same split, same
+#     rotation) and the rotated activations x @ H, both quantized along K.
+#  X6 forward: y = dq(Q(x H)) @ dq(Q(R))^T + (x @ down) @ up^T, the FP4 part
+#     exact on the dequantized values (the device accumulates in fp32), the
+#     low-rank part exact on the bf16 x.
+#  X7 reconstruct: W_hat = up @ down^T + dq(Q(R)) @ H.
+#  X8 packing: two nibbles per byte, even k in the low nibble (as R7);
+#     scales one byte per block, [rows][K/32].
+# ==========================================================================
+MX_BLOCK = 32
+E2M1_EMAX = 2
+
+
+def e2m1_values() -> np.ndarray:
+    """The 16 E2M1 code points by nibble (X1), from the format's definition:
+    exponent field 0 is subnormal (m * 2^(1-1) * 0.5), otherwise
+    2^(e-1) * (1 + m/2)."""
+    out = np.empty(16)
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+        out[c] = -mag if s else mag
+    return out
+
+
+def e2m1_encode(v) -> np.ndarray:
+    """X1/X4: nearest E2M1 value of each fp64 v (ties to the even mantissa,
+    saturating at 6); returns nibbles (uint8)."""
+    v = np.asarray(v, np.float64)
+    mags = e2m1_values()[:8]                       # nibbles 0..7, increasing
+    a = np.minimum(np.abs(v), 6.0)
+    d = np.abs(a[..., None] - mags)                # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    tie = d == best
+    # among equally near magnitudes take the even mantissa (nibble bit 0 clear)
+    even = tie & ((np.arange(8) & 1) == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(tie, axis=-1))
+    code = np.where((v < 0) & (code != 0), code | 8, code)
+    return code.astype(np.uint8)
+
+
+def mx_scale_exponent(absmax) -> np.ndarray:
+    """X3: E8M0 exponent byte of a block with the given absmax."""
+    a = np.asarray(absmax, np.float64)
+    e = np.zeros(a.shape, np.int64)
+    nz = a > 0
+    m, ex = np.frexp(a[nz])                        # a = m 2^ex, 0.5 <= m < 1
+    e[nz] = (ex - 1) - E2M1_EMAX + 127             # floor(log2 a) = ex - 1
+    return np.clip(e, 0, 254).astype(np.uint8)
+
+
+def mx_quantize(a):
+    """MXFP4 of rows of a [R,K] along K (X2-X4): (nibbles uint8 [R,K],
+    exponent bytes uint8 [R,K/32])."""
+    a = np.asarray(a, np.float64)
+    r, k = a.shape
+    if k % MX_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    if not np.all(np.isfinite(a)):
+        raise FloatingPointError("non-finite input")
+    blocks = a.reshape(r, k // MX_BLOCK, MX_BLOCK)
+    e = mx_scale_exponent(np.abs(blocks).max(axis=-1))
+    x = np.ldexp(1.0, 127 - e.astype(np.int64))    # 1 / block scale (a power of two)
+    codes = e2m1_encode(blocks * x[..., None]).reshape(r, k)
+    return codes, e
+
+
+def mx_dequant(codes, exps) -> np.ndarray:
+    """value = E2M1(nibble) * 2^(e - 127), exact in fp64."""
+    codes = np.asarray(codes, np.uint8)
+    r, k = codes.shape
+    v = e2m1_values()[codes].reshape(r, k // MX_BLOCK, MX_BLOCK)
+    s = np.ldexp(1.0, np.asarray(exps).astype(np.int64) - 127)
+    return (v * s[..., None]).reshape(r, k)
+
+
+def mx_pack(codes) -> np.ndarray:
+    """X8: two nibbles per byte, even k low."""
+    c = np.asarray(codes).astype(np.int64)
+    return ((c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)).astype(np.uint8)
+
+
+def mx_unpack(packed) -> np.ndarray:
+    p = np.asarray(packed, np.uint8).astype(np.int64)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def quantize_weight_mx(w, up, down):
+    """Builder of the FP4 mode (X5): MXFP4 of the rotated residual."""
+    return mx_quantize(residual(w, up, down))
+
+
+def quantize_act_mx(x):
+    """Activation half of the FP4 forward (X5): MXFP4 of x @ H."""
+    return mx_quantize(rotate(x))
+
+
+def forward_mx(x, wcodes, wexps, up, down) -> np.ndarray:
+    """X6 in fp64: the FP4 product on the dequantized operands plus the
+    low-rank branch on the unquantized activations."""
+    x = np.asarray(x, np.float64)
+    xc, xe = quantize_act_mx(x)
+    lr = (x @ np.asarray(down, np.float64)) @ np.asarray(up, np.float64).T
+    return mx_dequant(xc, xe) @ mx_dequant(wcodes, wexps).T + lr
+
+
+def reconstruct_mx(wcodes, wexps, up, down) -> np.ndarray:
+    """X7 in fp64."""
+    lr = np.asarray(up, np.float64) @ np.asarray(down, np.float64).T
+    return lr + rotate(mx_dequant(wcodes, wexps))
+
+
+MX_MARGIN = 1e-5     # relative distance from a rounding midpoint / a power of two
+
+
+def _e2m1_midpoints() -> np.ndarray:
+    m = e2m1_values()[:8]
+    return (m[1:] + m[:-1]) / 2.0
+
+
+def certify_mx(a, exps):
+    """(blocks_ok [R,K/32], near [R,K]) for MXFP4 of a with the given exponents:
+    a block is certified when its absmax is more than MX_MARGIN (relative)
+    from a power of two (where fp32 rounding of the input could move the
+    exponent); a value is near a tie when v / scale is within MX_MARGIN
+    (relative) of a rounding midpoint, where either neighbour is admissible."""
+    a = np.asarray(a, np.float64)
+    r, k = a.shape
+    blocks = a.reshape(r, k // MX_BLOCK, MX_BLOCK)
+    am = np.abs(blocks).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        l2 = np.log2(np.where(am > 0, am, 1.0))
+    ok = (np.abs(l2 - np.rint(l2)) > MX_MARGIN / np.log(2)) | (am == 0)
+    u = np.abs(blocks) * np.ldexp(1.0, 127 - np.asarray(exps).astype(np.int64))[..., None]
+    mids = _e2m1_midpoints()
+    near = (np.abs(u[..., None] - mids) <= MX_MARGIN * mids).any(axis=-1)
+    return ok, near.reshape(r, k)
+
+
+def check_device_mx(a, codes_dev, exps_dev):
+    """Compare a device MXFP4 quantization of a [R,K] with the oracle's.
+
+    Certified blocks must have the oracle's exponent and its nibbles except
+    at near-tie values (either neighbour).  Other blocks must be admissible:
+    the exponent one of the two a fp32 input could give (the oracle's or one
+    off), and the nibbles the oracle's encoding under the device's exponent,
+    near-ties either way.
+    """
+    a = np.asarray(a, np.float64)
+    r, k = a.shape
+    co, eo = mx_quantize(a)
+    ok, near = certify_mx(a, eo)
+    cd = np.asarray(codes_dev, np.uint8).reshape(r, k)
+    ed = np.asarray(exps_dev, np.uint8).reshape(r, k // MX_BLOCK)
+    vals = e2m1_values()
+
+    def codes_match(e_used, c_dev, near_mask):
+        ref = e2m1_encode(a * np.repeat(np.ldexp(1.0, 127 - e_used.astype(np.int64)), MX_BLOCK, axis=1))
+        same = c_dev == ref
+        # near a midpoint either neighbour: the device value must be one of the
+        # two grid values around the exact one
+        u = a * np.repeat(np.ldexp(1.0, 127 - e_used.astype(np.int64)), MX_BLOCK, axis=1)
+        dv = vals[c_dev]
+        mags = vals[:8]
+        au = np.minimum(np.abs(u), 6.0)
+        lo = mags[np.searchsorted(mags, au, side="right") - 1]
+        hi = mags[np.minimum(np.searchsorted(mags, au, side="left"), 7)]
+        nb = (np.abs(dv) == lo) | (np.abs(dv) == hi)
+        sign_ok = (dv == 0) | (np.sign(dv) == np.sign(u))
+        return (same | (near_mask & nb & sign_ok)).reshape(r, k // MX_BLOCK, MX_BLOCK).all(axis=-1)
+
+    cert_same = (ed == eo) & codes_match(eo, cd, near)
+    bad_cert = ok & ~cert_same
+    _, near_d = certify_mx(a, ed)
+    adm = (np.abs(ed.astype(np.int64) - eo.astype(np.int64)) <= 1) & codes_match(ed, cd, near_d)
+    bad_uncert = ~ok & ~cert_same & ~adm
+    return {
+        "blocks": int(ok.size),
+        "uncertified": int((~ok).sum()),
+        "differ": int((~cert_same).sum()),
+        "near_values": int(near.sum()),
+        "bad_certified": int(bad_cert.sum()),
+        "bad_uncertified": int(bad_uncert.sum()),
+        "ok": bool(bad_cert.sum() == 0 and bad_uncert.sum() == 0),
+    }

@@ -513,6 +513,134 @@ def pin_w8_certification():
     assert not O.check_device_quant_w8(r, res, qd, sd, fd)["ok"]
 
 
+# ----------------------------------------------------------------- MXFP4 mode
+# E2M1 code points as the OCP Microscaling Formats v1.0 specification lists
+# them (FP4 E2M1: +-0, 0.5, 1, 1.5, 2, 3, 4, 6), by nibble s e1 e0 m.
+OCP_E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def pin_mx_e2m1_table():
+    v = O.e2m1_values()
+    assert list(v[:8]) == OCP_E2M1
+    assert list(-v[8:]) == OCP_E2M1
+    # every code decodes and re-encodes to itself; -0 encodes as +0
+    codes = np.arange(16, dtype=np.uint8)
+    back = O.e2m1_encode(v)
+    assert np.array_equal(back[codes != 8], codes[codes != 8]) and back[8] == 0
+
+
+def pin_mx_encode_nearest_and_ties():
+    rng = np.random.default_rng(40)
+    v = np.concatenate([rng.uniform(-8, 8, 4000), rng.uniform(-0.6, 0.6, 1000)])
+    c = O.e2m1_encode(v)
+    dq = O.e2m1_values()[c]
+    grid = np.array(OCP_E2M1 + [-g for g in OCP_E2M1[1:]])
+    target = np.clip(v, -6, 6)                       # saturation
+    best = np.abs(target[:, None] - grid[None, :]).min(axis=1)
+    assert np.all(np.abs(target - dq) <= best + 1e-15)
+    # midpoints go to the even mantissa: 0.25->0, 0.75->1, 1.25->1, 1.75->2,
+    # 2.5->2, 3.5->4, 5->4; the sign follows
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    want = np.array([0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0])
+    assert np.array_equal(O.e2m1_values()[O.e2m1_encode(ties)], want)
+    assert np.array_equal(O.e2m1_values()[O.e2m1_encode(-ties)], -want)
+    assert O.e2m1_encode(np.array([-0.2]))[0] == 0    # rounds to zero: nibble 0
+
+
+def pin_mx_scale_rule():
+    rng = np.random.default_rng(41)
+    for p in (-20, -3, 0, 1, 5, 30):
+        blk = rng.uniform(-1, 1, (1, 32)) * 2.0 ** p
+        blk[0, 7] = 2.0 ** p                          # absmax exactly 2^p
+        c, e = O.mx_quantize(blk)
+        assert int(e[0, 0]) == p - 2 + 127
+        assert O.e2m1_values()[c[0, 7]] == 4.0        # 2^p / 2^(p-2)
+        blk[0, 7] = 6 * 2.0 ** p                      # 6 x 2^p is on the grid at e = p + 127
+        c, e = O.mx_quantize(blk)
+        assert int(e[0, 0]) == p + 127 and c[0, 7] == 7
+        # scaling the block by 2^k moves the exponent by k and keeps the nibbles
+        c2, e2 = O.mx_quantize(blk * 2.0 ** 9)
+        assert np.array_equal(c2, c) and int(e2[0, 0]) == int(e[0, 0]) + 9
+    c, e = O.mx_quantize(np.zeros((1, 32)))
+    assert e[0, 0] == 0 and not c.any()
+    c, e = O.mx_quantize(np.full((1, 32), 2.0 ** -140))
+    assert e[0, 0] == 0                               # clamped at the smallest scale
+
+
+def pin_mx_error_bound():
+    rng = np.random.default_rng(42)
+    a = rng.standard_normal((16, 256)) * np.exp(rng.standard_normal((16, 1)))
+    c, e = O.mx_quantize(a)
+    err = np.abs(O.mx_dequant(c, e) - a)
+    x = np.repeat(np.ldexp(1.0, e.astype(np.int64) - 127), 32, axis=1)
+    # half the largest grid spacing (4 -> 6) up to 6X; saturation above (< 8X)
+    assert np.all(np.where(np.abs(a) <= 6 * x, err <= x, err <= 2 * x))
+    # and the block maximum (in [4X, 8X)) keeps its sign and lands on 4 or 6
+    blocks = a.reshape(16, 8, 32)
+    i = np.abs(blocks).argmax(axis=-1)
+    top = np.take_along_axis(c.reshape(16, 8, 32), i[..., None], -1)[..., 0]
+    assert set(np.unique(top & 7)) <= {6, 7}
+
+
+def pin_mx_pack():
+    c = np.array([[1, 2, 15, 8, 0, 7]], dtype=np.uint8)
+    p = O.mx_pack(c)
+    assert list(p[0]) == [0x21, 0x8F, 0x70]
+    assert np.array_equal(O.mx_unpack(p), c)
+
+
+def pin_mx_forward_on_grid():
+    # activations whose rotation is exactly representable: the FP4 forward is
+    # then x @ W_hat^T with W_hat the MXFP4 reconstruct, to fp64 rounding
+    rng = np.random.default_rng(43)
+    m, n, k, r = 5, 24, 512, 4
+    grid = np.array(OCP_E2M1 + [-g for g in OCP_E2M1[1:]])
+    xh = grid[rng.integers(0, 15, (m, k))] * np.repeat(2.0 ** rng.integers(-6, 4, (m, k // 32)), 32, axis=1)
+    x = O.rotate(xh)
+    w = rng.standard_normal((n, k)) * 0.05
+    up = O.bf16_round(rng.standard_normal((n, r)) * 0.1)
+    dn = O.bf16_round(rng.standard_normal((k, r)) * 0.1)
+    wc, we = O.quantize_weight_mx(w, up, dn)
+    y = O.forward_mx(x, wc, we, up, dn)
+    ref = x @ O.reconstruct_mx(wc, we, up, dn).T
+    assert O.rel_fro(y, ref) < 1e-12
+    # the weight side alone: reconstruct recovers W up to the FP4 error of R
+    wh = O.reconstruct_mx(wc, we, up, dn)
+    e = O.residual(w, up, dn)
+    assert O.rel_fro(wh, w) <= 0.2 * np.linalg.norm(e) / np.linalg.norm(w) + 1e-12
+
+
+def pin_mx_layer():
+    from synth import gen_weight, gen_activations, bf16_bits_to_f32
+    rng = np.random.default_rng(44)
+    w = gen_weight(rng, 96, 512, 4).astype(np.float64)
+    x = bf16_bits_to_f32(gen_activations(rng, 16, 512, 0.01)).astype(np.float64)
+    up, dn = O.svd_init(w, 32)
+    wc, we = O.quantize_weight_mx(w, up, dn)
+    wh = O.reconstruct_mx(wc, we, up, dn)
+    res4 = O.quantize_residual(O.residual(w, up, dn), 32)
+    wh4 = O.reconstruct(res4.q, res4.scale, up, dn, 32)
+    e_mx, e_4 = O.rel_fro(wh, w), O.rel_fro(wh4, w)
+    assert e_4 < e_mx < 0.1          # the swept int4 grid beats the plain FP4 one
+    y = O.forward_mx(x, wc, we, up, dn)
+    assert O.cosine(y, x @ w.T) > 0.99
+
+
+def pin_mx_certification():
+    rng = np.random.default_rng(45)
+    a = rng.standard_normal((32, 256))
+    c, e = O.mx_quantize(a)
+    rep = O.check_device_mx(a, c, e)
+    assert rep["ok"] and rep["differ"] == 0
+    ok, near = O.certify_mx(a, e)
+    i, j = np.argwhere(~near)[0]
+    c2 = c.copy(); c2[i, j] = (c2[i, j] + 1) & 15 if (c2[i, j] & 7) < 7 else c2[i, j] - 1
+    assert not O.check_device_mx(a, c2, e)["ok"]
+    e2 = e.copy(); e2[i, j // 32] += 1
+    c3, _ = O.mx_quantize(a)
+    assert not O.check_device_mx(a, c3, e2)["ok"]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -586,7 +714,43 @@ def _mutations():
         up, dn = u[:, :rank] * s[:rank], vt[:rank].T * s[:rank]
         return (O.bf16_round(up), O.bf16_round(dn)) if round_bf16 else (up, dn)
 
+    orig_enc = O.sq_oracle.e2m1_encode
+    orig_mxe = O.sq_oracle.mx_scale_exponent
+    orig_mxdq = O.sq_oracle.mx_dequant
+
+    def e2m1_ties_away(v):
+        v = np.asarray(v, float)
+        c = orig_enc(v)
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+        up_one = np.isin(np.abs(v), mids)
+        bumped = np.where(up_one & ((c & 7) < 7), c + 1, c)
+        return np.where(up_one & (v < 0) & ((c & 7) == 0), 9, bumped).astype(np.uint8)
+
+    def mx_scale_ceil(a):
+        a = np.asarray(a, float)
+        e = orig_mxe(a).astype(np.int64)
+        with np.errstate(divide="ignore"):
+            frac = np.log2(np.where(a > 0, a, 1.0)) % 1 != 0
+        return np.clip(e + frac, 0, 254).astype(np.uint8)
+
+    def mx_scale_emax3(a):
+        return np.clip(orig_mxe(a).astype(np.int64) - 1, 0, 254).astype(np.uint8)
+
+    def mx_dequant_tiled(codes, exps):
+        codes = np.asarray(codes, np.uint8)
+        v = O.e2m1_values()[codes]
+        s = np.ldexp(1.0, np.asarray(exps).astype(np.int64) - 127)
+        return v * np.tile(s, (1, 32))
+
+    def act_unrotated(x):
+        return O.mx_quantize(np.asarray(x, float))
+
     return [
+        ("e2m1_encode", e2m1_ties_away),
+        ("mx_scale_exponent", mx_scale_ceil),
+        ("mx_scale_exponent", mx_scale_emax3),
+        ("mx_dequant", mx_dequant_tiled),
+        ("quantize_act_mx", act_unrotated),
         ("hadamard256", unnormalised),
         ("codes_for_scale", half_away),
         ("codes_for_scale", symmetric_clamp),
