@@ -205,6 +205,66 @@ sq_status_t sq_linear_fwd_w8(const uint16_t *x, int64_t m, const sq_w8_t *p, voi
                              sq_dtype_t y_dtype, void *workspace, size_t workspace_bytes,
                              void *stream);
 
+/* ------------------------------------------------------------------------
+ * MXFP4 mode (SquareQ README, "SquareQ v3 - W4", the "Residual codecs"
+ * bullet's FP4 alternative for native FP4 matrix instructions, and the
+ * op-level parity line that describes the FP4 forward as rotate +
+ * block-quant of the activations + FP4 product + epilogue).  The page's
+ * NVFP4 layout targets one vendor's instructions; this library uses the OCP
+ * MX counterpart that gfx950's scaled MFMA takes:
+ *   element  FP4 E2M1, magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}, nibble
+ *            s<<3 | e<<1 | m; a value that rounds to magnitude 0 is nibble 0
+ *   block    32 consecutive values along K share an E8M0 byte e (scale
+ *            2^(e-127)), e = floor(log2 absmax) - 2 + 127 clamped to [0, 254]
+ *            (0 for an all-zero block)
+ *   rounding v / 2^(e-127) to the nearest E2M1 value, ties to the even
+ *            mantissa, magnitudes above 6 saturate to 6
+ * The payload of one layer:
+ *   codes     uint8 [n][k/2]   two nibbles per byte, even k in the low nibble,
+ *                              coordinates after the rotation
+ *   exps      uint8 [n][k/32]  E8M0 block exponents
+ *   lora_up   bf16  [n][rank], lora_down bf16 [k][rank]  (rank 0, 16, 32, 64)
+ * `reserved` must be 0.  Shapes, alignment, streams and errors follow the W4
+ * conventions above. */
+typedef struct {
+  int64_t n, k;
+  int32_t rank, reserved;
+  uint8_t *codes;
+  uint8_t *exps;
+  uint16_t *lora_up;
+  uint16_t *lora_down;
+} sq_mx4_t;
+
+/* Builder side: codes/exps = MXFP4 of R = (w - lora_up @ lora_down^T) @ H,
+ * w fp32 [n][k].  Non-finite values of R set SQ_FLAG_NONFINITE in *dev_flags
+ * (outputs are then unspecified but written in bounds). */
+sq_status_t sq_quantize_weight_mx4(const float *w, const sq_mx4_t *p, int32_t *dev_flags,
+                                   void *stream);
+
+/* Activation half of the forward: xq [m][k/2] / xs [m][k/32] = MXFP4 of
+ * x @ H, x bf16 [m][k] (device buffers owned by the caller). */
+sq_status_t sq_quantize_act_mx4(const uint16_t *x, int64_t m, int64_t k, uint8_t *xq,
+                                uint8_t *xs, void *stream);
+
+/* w_hat[n][k] = bf16_round_nearest_even( lora_up @ lora_down^T + dq(codes, exps) @ H ),
+ * the rotation summed in fp32 (exact before the block scales), one rounding
+ * at the end. */
+sq_status_t sq_reconstruct_bf16_mx4(const sq_mx4_t *p, uint16_t *w_hat, void *stream);
+
+/* Forward: y[m][n] = sum_k dq(Q(x @ H))[m][k] dq(codes, exps)[n][k]
+ *                  + sum_r (x @ lora_down)[m][r] lora_up[n][r]
+ * with Q the MXFP4 quantization above (the activations are quantized inside
+ * the call, as sq_quantize_act_mx4 does), the FP4 product on
+ * v_mfma_scale_f32_16x16x128_f8f6f4 with fp32 accumulation, and the rank-r
+ * term from the unquantized x (fp32, carried as bf16 hi + lo).  y fp32 or
+ * bf16 (RNE of the fp32 result).  `workspace`: caller-owned device scratch
+ * of at least sq_linear_fwd_mx4_workspace_bytes(m, p) bytes; m == 0 is a
+ * no-op. */
+size_t sq_linear_fwd_mx4_workspace_bytes(int64_t m, const sq_mx4_t *p);
+sq_status_t sq_linear_fwd_mx4(const uint16_t *x, int64_t m, const sq_mx4_t *p, void *y,
+                              sq_dtype_t y_dtype, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
 /* Static description of a status code; never NULL. */
 const char *sq_status_str(sq_status_t status);
 int sq_abi_version(void);

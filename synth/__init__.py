@@ -123,3 +123,17 @@ def gen_payload_w8(rng: np.random.Generator, N: int, K: int, rank: int):
     up = f32_to_bf16_bits((rng.standard_normal((N, rank)) * (1.5 / np.sqrt(N))).astype(np.float32))
     down = f32_to_bf16_bits((rng.standard_normal((K, rank)) * (1.5 / np.sqrt(K))).astype(np.float32))
     return q, scales, up, down
+
+
+def gen_payload_mx(rng: np.random.Generator, N: int, K: int, rank: int):
+    """A random MXFP4 payload: uniform E2M1 nibbles packed two per byte
+    [N,K/2], E8M0 block exponents around those of an N(0,1/K) weight
+    (120 +- 1 at K = 6144, shifted with log2 K) [N,K/32], bf16 bits of up
+    [N,rank] and down [K,rank]."""
+    nib = rng.integers(0, 16, (N, K), dtype=np.uint8)
+    codes = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    base = int(round(127 - 2 - 0.5 * np.log2(K) + 1.3))
+    exps = (base + rng.integers(-1, 2, (N, K // 32))).astype(np.uint8)
+    up = f32_to_bf16_bits((rng.standard_normal((N, rank)) * (1.5 / np.sqrt(N))).astype(np.float32))
+    down = f32_to_bf16_bits((rng.standard_normal((K, rank)) * (1.5 / np.sqrt(K))).astype(np.float32))
+    return codes, exps, up, down

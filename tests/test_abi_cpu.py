@@ -149,3 +149,53 @@ def test_w8_other_arguments():
     ws = _lib.sq_linear_fwd_w8_workspace_bytes(4, p)
     assert _lib.sq_linear_fwd_w8(0x8000, 4, p, 0x9000, 0, 0xA000, ws - 1, None) == 6
     assert _lib.sq_reconstruct_bf16_w8(p, None, None) == 1
+
+
+# ------------------------------------------------------------------ MXFP4 mode
+def _payload_mx(n=16, k=256, rank=32, reserved=0, codes=0x1000, exps=0x2000, up=0x3000,
+                down=0x4000):
+    return _lib.SqMx4(n, k, rank, reserved, codes, exps, up, down)
+
+
+BAD_MX = [
+    ("k not multiple of 256", dict(k=288), 2),
+    ("n < 1", dict(n=0), 2),
+    ("rank 48", dict(rank=48), 4),
+    ("reserved set", dict(reserved=2), 4),
+    ("null codes", dict(codes=None), 1),
+    ("null exps", dict(exps=None), 1),
+    ("null up with rank", dict(up=None), 1),
+    ("misaligned exps", dict(exps=0x2001), 5),
+]
+
+
+@pytest.mark.parametrize("why,kw,status", BAD_MX, ids=[b[0] for b in BAD_MX])
+def test_mx_validation_before_launch(why, kw, status):
+    p = _payload_mx(**kw)
+    big = 1 << 40
+    assert _lib.sq_reconstruct_bf16_mx4(p, 0x5000, None) == status
+    assert _lib.sq_quantize_weight_mx4(0x6000, p, 0x7000, None) == status
+    assert _lib.sq_linear_fwd_mx4(0x8000, 4, p, 0x9000, 0, 0xA000, big, None) == status
+
+
+def test_mx_other_arguments():
+    p = _payload_mx()
+    big = 1 << 40
+    assert _lib.sq_quantize_weight_mx4(None, p, 0x7000, None) == 1
+    assert _lib.sq_quantize_weight_mx4(0x6000, p, None, None) == 1
+    assert _lib.sq_quantize_act_mx4(0x8000, 4, 300, 0x9000, 0xA000, None) == 2
+    assert _lib.sq_quantize_act_mx4(0x8000, -1, 256, 0x9000, 0xA000, None) == 2
+    assert _lib.sq_quantize_act_mx4(0x8000, 0, 256, None, None, None) == 0   # m == 0: no-op
+    assert _lib.sq_quantize_act_mx4(0x8000, 4, 256, None, 0xA000, None) == 1
+    assert _lib.sq_quantize_act_mx4(0x8000, 4, 256, 0x9004, 0xA000, None) == 5
+    assert _lib.sq_linear_fwd_mx4(0x8000, 0, p, 0x9000, 0, None, 0, None) == 0   # m == 0: no-op
+    assert _lib.sq_linear_fwd_mx4(0x8000, -1, p, 0x9000, 0, 0xA000, big, None) == 2
+    assert _lib.sq_linear_fwd_mx4(0x8000, 4, p, 0x9000, 9, 0xA000, big, None) == 7
+    ws = _lib.sq_linear_fwd_mx4_workspace_bytes(4, p)
+    assert ws >= 4 * 128 + 4 * 8                      # holds the FP4 activations and exponents
+    assert _lib.sq_linear_fwd_mx4(0x8000, 4, p, 0x9000, 0, 0xA000, ws - 1, None) == 6
+    assert _lib.sq_reconstruct_bf16_mx4(p, None, None) == 1
+    for rank in (0, 16, 32, 64):
+        pr = _payload_mx(rank=rank, up=None if rank == 0 else 0x3000,
+                         down=None if rank == 0 else 0x4000)
+        assert _lib.sq_linear_fwd_mx4_workspace_bytes(4, pr) > 0

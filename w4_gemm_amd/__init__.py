@@ -6,12 +6,16 @@ Entry points (C ABI in include/sq.h, same names here):
   sq_reconstruct_bf16  backward side: bf16 W_hat from the same payload
   sq_linear_dgrad      input gradient dx = dy W_hat straight from the payload
   *_w8                 the same for the int8-residual mode (int8 codes, one scale per row)
+  *_mx4                the MXFP4 mode (E2M1 codes, E8M0 block-32 exponents; the forward
+                       quantizes the rotated activations too and runs on FP4 MFMA)
 The rank-32 SVD split that feeds the quantizer is a host step (svd_init).
 """
 from .api import (W4Payload, dgrad_workspace_bytes, empty_payload, fwd_workspace_bytes,
                   linear_dgrad, linear_fwd, linear_fwd_contract, linear_fwd_rotate,
                   quantize_weight, reconstruct_bf16, W8Payload, empty_payload_w8,
-                  quantize_weight_w8, reconstruct_bf16_w8, fwd_w8_workspace_bytes, linear_fwd_w8)
+                  quantize_weight_w8, reconstruct_bf16_w8, fwd_w8_workspace_bytes, linear_fwd_w8,
+                  MX4Payload, empty_payload_mx4, quantize_weight_mx4, quantize_act_mx4,
+                  reconstruct_bf16_mx4, fwd_mx4_workspace_bytes, linear_fwd_mx4)
 from ._lib import SqError, abi_version
 from .svd_init import svd_init
 
@@ -19,4 +23,6 @@ __all__ = ["W4Payload", "empty_payload", "fwd_workspace_bytes", "linear_fwd", "l
            "linear_fwd_contract", "quantize_weight", "linear_dgrad", "dgrad_workspace_bytes",
            "reconstruct_bf16", "SqError", "abi_version", "svd_init", "W8Payload",
            "empty_payload_w8", "quantize_weight_w8", "reconstruct_bf16_w8",
-           "fwd_w8_workspace_bytes", "linear_fwd_w8"]
+           "fwd_w8_workspace_bytes", "linear_fwd_w8", "MX4Payload", "empty_payload_mx4",
+           "quantize_weight_mx4", "quantize_act_mx4", "reconstruct_bf16_mx4",
+           "fwd_mx4_workspace_bytes", "linear_fwd_mx4"]

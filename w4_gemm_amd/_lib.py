@@ -23,7 +23,9 @@ EXPORTS = ("sq_quantize_weight", "sq_linear_fwd_workspace_bytes", "sq_linear_fwd
            "sq_linear_fwd_rotate", "sq_linear_fwd_contract", "sq_reconstruct_bf16",
            "sq_linear_dgrad_workspace_bytes", "sq_linear_dgrad", "sq_status_str",
            "sq_abi_version", "sq_quantize_weight_w8_workspace_bytes", "sq_quantize_weight_w8",
-           "sq_reconstruct_bf16_w8", "sq_linear_fwd_w8_workspace_bytes", "sq_linear_fwd_w8")
+           "sq_reconstruct_bf16_w8", "sq_linear_fwd_w8_workspace_bytes", "sq_linear_fwd_w8",
+           "sq_quantize_weight_mx4", "sq_quantize_act_mx4", "sq_reconstruct_bf16_mx4",
+           "sq_linear_fwd_mx4_workspace_bytes", "sq_linear_fwd_mx4")
 
 
 class SqW4(ctypes.Structure):
@@ -49,6 +51,20 @@ class SqW8(ctypes.Structure):
         ("reserved", ctypes.c_int32),
         ("codes", ctypes.c_void_p),
         ("scales", ctypes.c_void_p),
+        ("lora_up", ctypes.c_void_p),
+        ("lora_down", ctypes.c_void_p),
+    ]
+
+
+class SqMx4(ctypes.Structure):
+    """Mirror of sq_mx4_t (MXFP4 mode)."""
+    _fields_ = [
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("rank", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("exps", ctypes.c_void_p),
         ("lora_up", ctypes.c_void_p),
         ("lora_down", ctypes.c_void_p),
     ]
@@ -101,6 +117,17 @@ def lib() -> ctypes.CDLL:
         L.sq_linear_fwd_w8_workspace_bytes.restype = ctypes.c_size_t
         L.sq_linear_fwd_w8.argtypes = [vp, i64, P8, vp, ctypes.c_int, vp, ctypes.c_size_t, vp]
         L.sq_linear_fwd_w8.restype = ctypes.c_int
+        PX = ctypes.POINTER(SqMx4)
+        L.sq_quantize_weight_mx4.argtypes = [vp, PX, vp, vp]
+        L.sq_quantize_weight_mx4.restype = ctypes.c_int
+        L.sq_quantize_act_mx4.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.sq_quantize_act_mx4.restype = ctypes.c_int
+        L.sq_reconstruct_bf16_mx4.argtypes = [PX, vp, vp]
+        L.sq_reconstruct_bf16_mx4.restype = ctypes.c_int
+        L.sq_linear_fwd_mx4_workspace_bytes.argtypes = [i64, PX]
+        L.sq_linear_fwd_mx4_workspace_bytes.restype = ctypes.c_size_t
+        L.sq_linear_fwd_mx4.argtypes = [vp, i64, PX, vp, ctypes.c_int, vp, ctypes.c_size_t, vp]
+        L.sq_linear_fwd_mx4.restype = ctypes.c_int
         L.sq_status_str.argtypes = [ctypes.c_int]
         L.sq_status_str.restype = ctypes.c_char_p
         L.sq_abi_version.argtypes = []
@@ -177,3 +204,25 @@ def sq_linear_fwd_w8(x, m: int, p: SqW8, y, y_dtype: int, workspace, workspace_b
                      stream) -> int:
     return lib().sq_linear_fwd_w8(x, m, ctypes.byref(p), y, y_dtype, workspace, workspace_bytes,
                                   stream)
+
+
+def sq_quantize_weight_mx4(w, p: SqMx4, dev_flags, stream) -> int:
+    return lib().sq_quantize_weight_mx4(w, ctypes.byref(p), dev_flags, stream)
+
+
+def sq_quantize_act_mx4(x, m: int, k: int, xq, xs, stream) -> int:
+    return lib().sq_quantize_act_mx4(x, m, k, xq, xs, stream)
+
+
+def sq_reconstruct_bf16_mx4(p: SqMx4, w_hat, stream) -> int:
+    return lib().sq_reconstruct_bf16_mx4(ctypes.byref(p), w_hat, stream)
+
+
+def sq_linear_fwd_mx4_workspace_bytes(m: int, p: SqMx4) -> int:
+    return lib().sq_linear_fwd_mx4_workspace_bytes(m, ctypes.byref(p))
+
+
+def sq_linear_fwd_mx4(x, m: int, p: SqMx4, y, y_dtype: int, workspace, workspace_bytes: int,
+                      stream) -> int:
+    return lib().sq_linear_fwd_mx4(x, m, ctypes.byref(p), y, y_dtype, workspace, workspace_bytes,
+                                   stream)

@@ -11,7 +11,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import SqError, SqW4, SqW8, SQ_BF16, SQ_F32
+from ._lib import SqError, SqMx4, SqW4, SqW8, SQ_BF16, SQ_F32
 
 
 @dataclass
@@ -251,4 +251,100 @@ def linear_fwd_w8(x: torch.Tensor, p: W8Payload, out_dtype=torch.float32,
     _check(_lib.sq_linear_fwd_w8(x.data_ptr(), m, p.abi(), out.data_ptr(), dt,
                                  workspace.data_ptr(), workspace.numel(), _stream()),
            "sq_linear_fwd_w8")
+    return out
+
+
+# ---------------------------------------------------------------- MXFP4 mode
+@dataclass
+class MX4Payload:
+    """Device tensors of one MXFP4 layer (layouts as in sq.h)."""
+    codes: torch.Tensor      # uint8 [N, K/2] E2M1 nibbles
+    exps: torch.Tensor       # uint8 [N, K/32] E8M0 block exponents
+    up: torch.Tensor | None  # bfloat16 [N, rank]
+    down: torch.Tensor | None  # bfloat16 [K, rank]
+
+    @property
+    def n(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def k(self) -> int:
+        return self.codes.shape[1] * 2
+
+    @property
+    def rank(self) -> int:
+        return 0 if self.up is None else self.up.shape[1]
+
+    def abi(self) -> SqMx4:
+        _require(self.codes, torch.uint8, "codes")
+        _require(self.exps, torch.uint8, "exps")
+        if self.up is not None:
+            _require(self.up, torch.bfloat16, "up")
+            _require(self.down, torch.bfloat16, "down")
+        return SqMx4(self.n, self.k, self.rank, 0, _ptr(self.codes), _ptr(self.exps),
+                     _ptr(self.up), _ptr(self.down))
+
+
+def empty_payload_mx4(n: int, k: int, rank: int, device="cuda") -> MX4Payload:
+    up = torch.empty((n, rank), dtype=torch.bfloat16, device=device) if rank else None
+    down = torch.empty((k, rank), dtype=torch.bfloat16, device=device) if rank else None
+    return MX4Payload(torch.empty((n, k // 2), dtype=torch.uint8, device=device),
+                      torch.empty((n, k // 32), dtype=torch.uint8, device=device), up, down)
+
+
+def quantize_weight_mx4(w: torch.Tensor, up: torch.Tensor | None, down: torch.Tensor | None):
+    """sq_quantize_weight_mx4: fp32 W [N,K] and bf16 factors -> (payload, flags tensor)."""
+    _require(w, torch.float32, "w")
+    n, k = w.shape
+    rank = 0 if up is None else up.shape[1]
+    p = empty_payload_mx4(n, k, rank, w.device)
+    p.up, p.down = up, down
+    flags = torch.zeros(4, dtype=torch.int32, device=w.device)
+    _check(_lib.sq_quantize_weight_mx4(w.data_ptr(), p.abi(), flags.data_ptr(), _stream()),
+           "sq_quantize_weight_mx4")
+    return p, flags
+
+
+def quantize_act_mx4(x: torch.Tensor):
+    """sq_quantize_act_mx4: bf16 x [M,K] -> (uint8 codes [M,K/2], uint8 exps [M,K/32]) of x @ H."""
+    _require(x, torch.bfloat16, "x")
+    m, k = x.shape
+    xq = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
+    xs = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
+    _check(_lib.sq_quantize_act_mx4(x.data_ptr(), m, k, xq.data_ptr(), xs.data_ptr(), _stream()),
+           "sq_quantize_act_mx4")
+    return xq, xs
+
+
+def reconstruct_bf16_mx4(p: MX4Payload, out: torch.Tensor | None = None):
+    """sq_reconstruct_bf16_mx4: MXFP4 payload -> bf16 W_hat [N,K]."""
+    if out is None:
+        out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device=p.codes.device)
+    _require(out, torch.bfloat16, "out")
+    _check(_lib.sq_reconstruct_bf16_mx4(p.abi(), out.data_ptr(), _stream()),
+           "sq_reconstruct_bf16_mx4")
+    return out
+
+
+def fwd_mx4_workspace_bytes(m: int, p: MX4Payload) -> int:
+    return _lib.sq_linear_fwd_mx4_workspace_bytes(m, p.abi())
+
+
+def linear_fwd_mx4(x: torch.Tensor, p: MX4Payload, out_dtype=torch.float32,
+                   workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """sq_linear_fwd_mx4: bf16 x [M,K] -> y [M,N] (fp32 or bf16) for an MXFP4 payload."""
+    _require(x, torch.bfloat16, "x")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, p.n), dtype=out_dtype, device=x.device)
+    _require(out, out.dtype, "out")
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (m, p.n):
+        raise ValueError("out must be fp32 or bf16 of shape [M, N]")
+    dt = SQ_BF16 if out.dtype == torch.bfloat16 else SQ_F32
+    nbytes = fwd_mx4_workspace_bytes(m, p)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    _check(_lib.sq_linear_fwd_mx4(x.data_ptr(), m, p.abi(), out.data_ptr(), dt,
+                                  workspace.data_ptr(), workspace.numel(), _stream()),
+           "sq_linear_fwd_mx4")
     return out

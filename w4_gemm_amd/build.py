@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libsq.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["sq_abi.hip", "sq_reconstruct.hip", "sq_quantize.hip", "sq_fwd.hip", "sq_dgrad.hip",
-           "sq_decode.hip", "sq_w8.hip"]
+           "sq_decode.hip", "sq_w8.hip", "sq_mx.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -55,6 +55,18 @@ sq_status_t check_payload_w8(const sq_w8_t* p) {
   return SQ_OK;
 }
 
+sq_status_t check_payload_mx(const sq_mx4_t* p) {
+  if (!p) return SQ_E_NULL;
+  if (p->k < 256 || p->k % 256 != 0 || p->n < 1) return SQ_E_SHAPE;
+  if ((p->rank != 0 && p->rank != 16 && p->rank != 32 && p->rank != 64) || p->reserved != 0)
+    return SQ_E_RANK;
+  if (!p->codes || !p->exps) return SQ_E_NULL;
+  if (p->rank > 0 && (!p->lora_up || !p->lora_down)) return SQ_E_NULL;
+  if (!aligned16(p->codes) || !aligned16(p->exps)) return SQ_E_ALIGN;
+  if (p->rank > 0 && (!aligned16(p->lora_up) || !aligned16(p->lora_down))) return SQ_E_ALIGN;
+  return SQ_OK;
+}
+
 sq_status_t from_hip(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_E_HIP; }
 
 }  // namespace
@@ -262,6 +274,63 @@ sq_status_t sq_linear_fwd_w8(const uint16_t* x, int64_t m, const sq_w8_t* p, voi
   return from_hip(sq::launch_fwd_contract(plan, reinterpret_cast<const uint8_t*>(p->codes),
                                           p->scales, p->lora_up, y, y_dtype == SQ_BF16, workspace,
                                           s));
+}
+
+// ---------------------------------------------------------------- MXFP4 mode
+sq_status_t sq_quantize_weight_mx4(const float* w, const sq_mx4_t* p, int32_t* dev_flags,
+                                   void* stream) {
+  sq_status_t st = check_payload_mx(p);
+  if (st != SQ_OK) return st;
+  if (!w || !dev_flags) return SQ_E_NULL;
+  if (!aligned16(w) || !aligned16(dev_flags)) return SQ_E_ALIGN;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_quantize_mx(w, p->lora_up, p->lora_down, p->codes, p->exps, dev_flags,
+                                         p->n, p->k, p->rank, static_cast<hipStream_t>(stream)));
+}
+
+sq_status_t sq_quantize_act_mx4(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq, uint8_t* xs,
+                                void* stream) {
+  if (m < 0 || k < 256 || k % 256 != 0) return SQ_E_SHAPE;
+  if (m == 0) return SQ_OK;
+  if (!x || !xq || !xs) return SQ_E_NULL;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(xs)) return SQ_E_ALIGN;
+  sq_status_t st = check_device();
+  if (st != SQ_OK) return st;
+  return from_hip(sq::launch_quantize_act_mx(x, m, k, xq, xs, static_cast<hipStream_t>(stream)));
+}
+
+sq_status_t sq_reconstruct_bf16_mx4(const sq_mx4_t* p, uint16_t* w_hat, void* stream) {
+  sq_status_t st = check_payload_mx(p);
+  if (st != SQ_OK) return st;
+  if (!w_hat) return SQ_E_NULL;
+  if (!aligned16(w_hat)) return SQ_E_ALIGN;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_reconstruct_mx(p->codes, p->exps, p->lora_up, p->lora_down, w_hat,
+                                            p->n, p->k, p->rank,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+size_t sq_linear_fwd_mx4_workspace_bytes(int64_t m, const sq_mx4_t* p) {
+  if (!p || m <= 0 || p->k < 256 || p->k % 256 || p->n < 1) return 0;
+  return sq::plan_mx(m, p->n, p->k, p->rank).total;
+}
+
+sq_status_t sq_linear_fwd_mx4(const uint16_t* x, int64_t m, const sq_mx4_t* p, void* y,
+                              sq_dtype_t y_dtype, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (y_dtype != SQ_F32 && y_dtype != SQ_BF16) return SQ_E_DTYPE;
+  sq_status_t st = check_payload_mx(p);
+  if (st != SQ_OK) return st;
+  if (m < 0) return SQ_E_SHAPE;
+  if (m == 0) return SQ_OK;
+  if (!x || !y || !workspace) return SQ_E_NULL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace)) return SQ_E_ALIGN;
+  const sq::MxPlan plan = sq::plan_mx(m, p->n, p->k, p->rank);
+  if (workspace_bytes < plan.total) return SQ_E_WORKSPACE;
+  if ((st = check_device()) != SQ_OK) return st;
+  return from_hip(sq::launch_fwd_mx(plan, x, p->codes, p->exps, p->lora_up, p->lora_down, y,
+                                    y_dtype == SQ_BF16, workspace,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -22,6 +22,27 @@ hipError_t launch_quantize_w8(const float* w, const uint16_t* up, const uint16_t
                               int64_t n, int64_t k, int rank, void* workspace,
                               hipStream_t stream);
 
+// MXFP4 mode: E2M1 codes [rows][K/2] (even k in the low nibble) with E8M0
+// block-32 exponents [rows][K/32].
+struct MxPlan {
+  int64_t m, n, k;
+  int rank;
+  int slices;   // workgroups along K of the activation pass (4 blocks each)
+  size_t off_xq, off_xs, off_downT, off_tpart, off_thi, off_tlo, total;
+};
+MxPlan plan_mx(int64_t m, int64_t n, int64_t k, int rank);
+hipError_t launch_quantize_mx(const float* w, const uint16_t* up, const uint16_t* down,
+                              uint8_t* codes, uint8_t* exps, int32_t* flags, int64_t n, int64_t k,
+                              int rank, hipStream_t stream);
+hipError_t launch_quantize_act_mx(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq, uint8_t* xs,
+                                  hipStream_t stream);
+hipError_t launch_fwd_mx(const MxPlan& p, const uint16_t* x, const uint8_t* wq, const uint8_t* wsc,
+                         const uint16_t* up, const uint16_t* down, void* y, int y_bf16,
+                         void* workspace, hipStream_t stream);
+hipError_t launch_reconstruct_mx(const uint8_t* codes, const uint8_t* exps, const uint16_t* up,
+                                 const uint16_t* down, uint16_t* w_hat, int64_t n, int64_t k,
+                                 int rank, hipStream_t stream);
+
 // Forward: workspace layout and launch.
 struct FwdPlan {
   int64_t m, n, k;
