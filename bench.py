@@ -28,7 +28,9 @@ wall time on a two-layer fp32 checkpoint, the small-M forward sweep (M = 1, 16, 
 6144x16384 g32 weight) in GB/s of bytes the call must move, the
 rotation, reconstruct and quantize kernels against HBM peak, and the
 int8-residual mode (rank 16, one int8 code per weight and one fp16 scale
-per row) at the same shape: its forward, reconstruct and quantizer.
+per row) and the MXFP4 mode (rank 32, E2M1 codes with E8M0 block-32
+exponents, FP4 x FP4 forward on the scaled MFMA, against the 10.1 PFLOP/s
+dense FP4 peak) at the same shape: forward, reconstruct and quantizer.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 4]
        python bench.py --ops copy      (the counter calibration copy only)
@@ -48,6 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_F16_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense FP4 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 PEAK_VALU_TOPS = 39.32        # non-packed vector lane-ops: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 SWEEP_OPS_PER_ELEMENT = 31 * 5
@@ -89,7 +92,7 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--ops", default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs,w8")
+    ap.add_argument("--ops", default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs,w8,mx")
     ap.add_argument("--small-m", default="1,16,128")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -210,6 +213,9 @@ def main():
     # ---------------------------------------------------------------- int8-residual mode
     if "w8" in ops:
         res["w8"] = w8_run(torch, W, dev, w, x, what, M, N, K, args.steps, args.warmup)
+    # ---------------------------------------------------------------- MXFP4 mode
+    if "mx" in ops:
+        res["mx"] = mx_run(torch, W, dev, w, x, up, down, what, M, N, K, args.steps, args.warmup)
     # ---------------------------------------------------------------- streaming builder
     if "builder" in ops:
         res["builder"] = builder_run(torch, dev)
@@ -278,6 +284,8 @@ def main():
         out["builder"] = res["builder"]
     if "w8" in res:
         out["w8"] = res["w8"]
+    if "mx" in res:
+        out["mx"] = res["mx"]
     if "smallm" in res:
         out["fwd_small_m"] = res["smallm"]
     if "configs" in res:
@@ -359,6 +367,50 @@ def w8_run(torch, W, dev, w, x, what, M, N, K, steps, warmup):
     out["fwd_pct_bf16_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_F16_TFLOPS
     out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
     del pays, p0, qws, ws, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def mx_run(torch, W, dev, w, x, up, down, what, M, N, K, steps, warmup):
+    """The MXFP4 mode at the same layer shape with the same rank-32 factors:
+    sq_quantize_weight_mx4 of the same weight, then sq_linear_fwd_mx4 (whole
+    call: activation rotation + FP4 quantization + low-rank projection, FP4
+    contraction) and sq_reconstruct_bf16_mx4 (rotating over three
+    payload/output sets), each timed with HIP events."""
+    R = up.shape[1]
+    p0, flags = W.quantize_weight_mx4(w, up, down)
+    torch.cuda.synchronize()
+    assert int(flags[0]) == 0, "FP4 quantizer flagged the synthetic weight"
+    pays = [p0] + [W.MX4Payload(p0.codes.clone(), p0.exps.clone(), up, down) for _ in range(2)]
+    ws = torch.empty(W.fwd_mx4_workspace_bytes(M, p0), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for i in range(warmup):
+            fn(i)
+        marks = [(ev(), ev()) for _ in range(steps)]
+        for i, (a, b) in enumerate(marks):
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in marks]))
+
+    t_fwd = timed(lambda i: W.linear_fwd_mx4(x, p0, out=y, workspace=ws))
+    t_rec = timed(lambda i: W.reconstruct_bf16_mx4(pays[i % 3], out=what[i % 3]))
+    t_q = timed(lambda i: W.quantize_weight_mx4(w, up, down))
+    flops = 2.0 * M * N * K + 2.0 * M * R * (N + K)
+    pay = N * K / 2 + N * K / 32 + (N + K) * R * 2
+    rec_bytes = pay + 2.0 * N * K
+    out = {"rank": R, "fwd_ms": t_fwd, "fwd_tflops": flops / (t_fwd * 1e-3) / 1e12,
+           "reconstruct_ms": t_rec, "reconstruct_gbps": rec_bytes / (t_rec * 1e-3) / 1e9,
+           "quantize_ms": t_q}
+    out["fwd_pct_fp4_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_FP4_TFLOPS
+    out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
+    del pays, p0, ws, y
     torch.cuda.empty_cache()
     return out
 

@@ -20,7 +20,7 @@
 //   k_mx_tsum          t = sum of the partials in order, split into bf16 hi + lo
 //   k_mx_gemm          the FP4 x FP4 product on v_mfma_scale_f32_16x16x128_f8f6f4
 //                      plus the rank-r branch, fp32 or bf16 out
-//   k_mx_reconstruct   bf16 W_hat
+// and bf16 W_hat from the strip kernel of the reconstruct (group code 1).
 #include <algorithm>
 
 #include "sq_device.hpp"
@@ -411,6 +411,51 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
     }
   }
   // acc[i][j][v]: row rbase + 16 i + 4 g + v, column cbase + 16 j + fr
+  if (y_bf16) {
+    // Each wave stages 64 x 64 bf16 (8 KB, 128-byte rows with the chunk
+    // swizzle of the W4 kernels) in its own part of the stage buffers, twice,
+    // and stores eight whole 128-byte row segments per instruction.
+    __syncthreads();   // every wave is done with the stage buffers
+    const int wb = wave >> 1;
+    uint8_t* st = (wb == 0 ? mx_a0 : wb == 1 ? mx_a1 : wb == 2 ? mx_b0 : mx_b1) + (wave & 1) * 8192;
+    const bool full_cols = (cbase + 64 <= n) && ((n & 7) == 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int lrow = 16 * i + 4 * g + v;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = 16 * j + fr;   // chunk col/8, element col%8
+            *reinterpret_cast<uint16_t*>(st + lrow * 128 + 16 * ((col >> 3) ^ a_swz(lrow)) +
+                                         2 * (col & 7)) = f32_to_bf16(acc[4 * h + i][j][v]);
+          }
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int lrow = 8 * it + (lane >> 3), chunk = lane & 7;
+        const int64_t r = rbase + 64 * h + lrow, c = cbase + 8 * chunk;
+        const u32x4 o = *reinterpret_cast<const u32x4*>(st + lrow * 128 + 16 * (chunk ^ a_swz(lrow)));
+        if (r >= m) continue;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(y) + r * n + c;
+        if (full_cols) {
+          *reinterpret_cast<u32x4*>(dst) = o;
+        } else {
+          const uint16_t* hv = reinterpret_cast<const uint16_t*>(&o);
+          for (int e = 0; e < 8 && c + e < n; ++e) dst[e] = hv[e];
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // the reads are done before the next pass writes
+      __builtin_amdgcn_wave_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -420,90 +465,9 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int64_t c = cbase + 16 * j + fr;
-        if (c >= n) continue;
-        if (y_bf16)
-          reinterpret_cast<uint16_t*>(y)[r * n + c] = f32_to_bf16(acc[i][j][v]);
-        else
-          reinterpret_cast<float*>(y)[r * n + c] = acc[i][j][v];
+        if (c < n) reinterpret_cast<float*>(y)[r * n + c] = acc[i][j][v];
       }
     }
-}
-
-// ---------------------------------------------------------------- reconstruct
-// One wave per 16 rows x one 256-column block (the lane holds 64 consecutive
-// columns: two MX blocks).  Each nibble becomes 2 * |E2M1| (an integer in
-// {0, 1, 2, 3, 4, 6, 8, 12}) through a byte-table permute and then a signed
-// fp32; five in-lane butterfly stages run on these exact integers, the sixth
-// joins the two blocks with their scales (s * 2^-5 each: the 1/2 of the
-// doubling and the 1/16 of H), and the two cross-lane stages follow.  The
-// rank-r term is added on bf16 MFMA as in the quantizer, then the tile is
-// rounded to bf16 and stored.
-__global__ void __launch_bounds__(256) k_mx_reconstruct(
-    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ exps,
-    const uint16_t* __restrict__ up, const uint16_t* __restrict__ down,
-    uint16_t* __restrict__ w_hat, int64_t n, int64_t k, int rank) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t nblk = k >> 8;
-  const int64_t blk = (int64_t)blockIdx.y * 4 + wave;
-  const int64_t row0 = (int64_t)blockIdx.x * 16;
-  if (blk >= nblk) return;
-  const int c = lane & 15, g = lane >> 4;
-  const int64_t row = min(row0 + c, n - 1);
-  const int64_t col = blk * 256 + 64 * g;
-
-  const u32x4* src = reinterpret_cast<const u32x4*>(codes + row * (k >> 1) + (col >> 1));
-  const u32x4 w0 = src[0], w1 = src[1];
-  const uint32_t e2 = *reinterpret_cast<const uint16_t*>(exps + row * (k >> 5) + (col >> 5));
-  float v[64];
-  // bytes {0,1,2,3} and {4,6,8,12}: 2 * |E2M1| by magnitude nibble
-  constexpr uint32_t TLO = 0x03020100u, THI = 0x0C080604u;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t word = j < 4 ? w0[j] : w1[j - 4];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const uint32_t nib = (word >> (4 * half)) & 0x0F0F0F0Fu;   // elements 2b + half
-      const uint32_t mags = __builtin_amdgcn_perm(THI, TLO, nib & 0x07070707u);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float mag = (float)((mags >> (8 * b)) & 0xFFu);
-        const uint32_t sgn = (nib >> (8 * b + 3)) & 1u;
-        v[8 * j + 2 * b + half] = __uint_as_float(__float_as_uint(mag) | (sgn << 31));
-      }
-    }
-  }
-  // column bits 0..4 (inside one MX block): exact integer sums (|.| <= 384)
-#pragma unroll
-  for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if (i & h) continue;
-      const float a = v[i], b = v[i + h];
-      v[i] = a + b;
-      v[i + h] = a - b;
-    }
-  }
-  // column bit 5 joins the two blocks with their scales 2^(e-127) / 32
-  const float s_lo = __uint_as_float(max((int)(e2 & 0xFFu) - 5, 0) << 23);
-  const float s_hi = __uint_as_float(max((int)(e2 >> 8) - 5, 0) << 23);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float a = v[i] * s_lo, b = v[i + 32] * s_hi;
-    v[i] = a + b;
-    v[i + 32] = a - b;
-  }
-  fwht_cross64(v, lane);
-  lowrank_acc_16x256(v, up, down, row0, n, blk * 256, rank, false, lane);
-  if (row0 + c >= n) return;
-  u32x4* dst = reinterpret_cast<u32x4*>(w_hat + (row0 + c) * k + col);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(v[8 * j + 2 * e], v[8 * j + 2 * e + 1]);
-    dst[j] = o;
-  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -580,13 +544,13 @@ hipError_t launch_fwd_mx(const MxPlan& p, const uint16_t* x, const uint8_t* wq, 
   return hipGetLastError();
 }
 
+// The reconstruct runs in the strip kernel of the W4 payload (group code 1):
+// an exponent row indexes like a row of group-64 fp16 scales.
 hipError_t launch_reconstruct_mx(const uint8_t* codes, const uint8_t* exps, const uint16_t* up,
                                  const uint16_t* down, uint16_t* w_hat, int64_t n, int64_t k,
                                  int rank, hipStream_t stream) {
-  dim3 grid((unsigned)((n + 15) / 16), (unsigned)(((k >> 8) + 3) / 4));
-  hipLaunchKernelGGL(k_mx_reconstruct, grid, dim3(256), 0, stream, codes, exps, up, down, w_hat, n,
-                     k, rank);
-  return hipGetLastError();
+  return launch_reconstruct(codes, reinterpret_cast<const uint16_t*>(exps), up, down, w_hat, n, k,
+                            1, rank, stream);
 }
 
 }  // namespace sq

@@ -20,7 +20,10 @@
 // The same kernel rebuilds the int8-residual mode (SquareQ README, "v3.1 -
 // int8-residual mode"; GROUP = 0 selects it): 64 bytes of codes per lane
 // and strip, one scale per row, the butterflies on exact integers in fp32
-// and the scale applied once after the last stage.
+// and the scale applied once after the last stage.  GROUP = 1 selects the
+// MXFP4 payload (E2M1 nibbles with one E8M0 byte per 32 values, whose
+// per-row layout indexes like group-64 fp16 scales: one 16-bit word per 64
+// values holds the two exponents).
 #include "sq_device.hpp"
 #include "sq_kernels.h"
 
@@ -42,16 +45,34 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 // groups and is done as fp32 y = s_lo * a +- (s_hi * b), with the fp16
 // operands converted inside the mixed-precision FMA; s * b is exact in fp32
 // (11-bit times 8-bit significands) and each output is rounded once.
+//
+// MX = true reads E2M1 nibbles instead: a byte-table permute turns the two
+// magnitude fields into 2|v| (an integer in {0, 1, 2, 3, 4, 6, 8, 12}) under
+// the fp16 exponent of 1024, one packed subtraction leaves the integer, and
+// the nibbles' sign bits move into the fp16 sign bits; the scales then carry
+// the factor 1/2.
+template <bool MX>
 __device__ __forceinline__ void dequant_rotate64(float (&v)[64], const u32x4 (&w)[2], float s_lo,
                                                  float s_hi) {
   half2_t h[32];   // h[4j + p] = (element 8j+p, element 8j+p+4)
+  constexpr uint32_t TLO = 0x03020100u, THI = 0x0C080604u;   // 2|E2M1| by magnitude
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t word = w[j >> 2][j & 3];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const uint32_t bits = ((word >> (4 * p)) & 0x000F000Fu) ^ 0x64086408u;
-      h[4 * j + p] = __builtin_bit_cast(half2_t, bits) - (half2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+      if constexpr (MX) {
+        const uint32_t sh = word >> (4 * p);
+        // selector bytes 1 and 3 are zero: they pick the table's 0
+        const uint32_t mags = __builtin_amdgcn_perm(THI, TLO, sh & 0x00070007u);
+        const half2_t a = __builtin_bit_cast(half2_t, mags | 0x64006400u) -
+                          (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
+        h[4 * j + p] = __builtin_bit_cast(
+            half2_t, __builtin_bit_cast(uint32_t, a) ^ ((sh << 12) & 0x80008000u));
+      } else {
+        const uint32_t bits = ((word >> (4 * p)) & 0x000F000Fu) ^ 0x64086408u;
+        h[4 * j + p] = __builtin_bit_cast(half2_t, bits) - (half2_t){(_Float16)1032.0f, (_Float16)1032.0f};
+      }
     }
   }
   // column bits 0, 1 (p) and 3, 4 (j bits 0, 1): pairs of registers
@@ -169,6 +190,8 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
     const uint16_t* __restrict__ up, const uint16_t* __restrict__ down,
     uint16_t* __restrict__ w_hat, int64_t n, int64_t k, int strips) {
   constexpr bool W8 = GROUP == 0;
+  constexpr bool MX = GROUP == 1;
+  constexpr int SG = MX ? 64 : (GROUP > 0 ? GROUP : 1);   // values per 16-bit scale word
   constexpr int RC = (RANK + 31) / 32;   // rank-32 chunks (rank 16: the upper half reads zero)
   // A operands of the low-rank MFMA for the block, in fragment order
   // [chunk][t][lane] so that every read is 64 consecutive 16-byte slots.
@@ -200,12 +223,12 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
   __syncthreads();
   if (first >= nstr) return;
 
-  const int64_t spr = W8 ? 1 : k / (GROUP > 0 ? GROUP : 1);   // scales per row
+  const int64_t spr = W8 ? 1 : k / SG;   // scale words per row
   const int64_t cpr = W8 ? k : k >> 1;                        // code bytes per row
   // byte offset of the lane's 16-byte store piece from the strip's first row
   const uint32_t stoff = 2u * ((uint32_t)((lane >> 5) * k) + (uint32_t)(blk * 256) + 8u * (lane & 31));
   const uint8_t* cblk = codes + blk * (W8 ? 256 : 128);
-  const uint16_t* sblk = scales + (W8 ? 0 : blk * (256 / (GROUP > 0 ? GROUP : 1)));
+  const uint16_t* sblk = scales + (W8 ? 0 : blk * (256 / SG));
   u32x4* stage = &s_stage[wave][0];
   // the lane's row of strip st, clamped to the last row
   auto lrow = [&](int64_t st) { return min(st * 16 + c, n - 1); };
@@ -256,9 +279,14 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
       const float s16 = fp16_bits_to_f32(in.s2) * 0.0625f;
 #pragma unroll
       for (int e = 0; e < 64; ++e) v[e] *= s16;
+    } else if constexpr (MX) {
+      // 2^(e-127) x 1/2 x 1/16 = 2^(e-132), flushed to 0 below the fp32 normals
+      dequant_rotate64<true>(v, in.w, __uint_as_float((uint32_t)max((int)(in.s2 & 0xFFu) - 5, 0) << 23),
+                             __uint_as_float((uint32_t)max((int)((in.s2 >> 8) & 0xFFu) - 5, 0) << 23));
+      fwht_cross64_swap(v);
     } else {
-      dequant_rotate64(v, in.w, fp16_bits_to_f32(in.s2 & 0xFFFFu) * 0.0625f,
-                       fp16_bits_to_f32(in.s2 >> 16) * 0.0625f);
+      dequant_rotate64<false>(v, in.w, fp16_bits_to_f32(in.s2 & 0xFFFFu) * 0.0625f,
+                              fp16_bits_to_f32(in.s2 >> 16) * 0.0625f);
       fwht_cross64_swap(v);
     }
 #pragma unroll
@@ -305,6 +333,9 @@ static void launch_rank(dim3 grid, int group, hipStream_t stream, const uint8_t*
                         uint16_t* w_hat, int64_t n, int64_t k, int s) {
   if (group == 0)
     hipLaunchKernelGGL((k_reconstruct<RANK, 0>), grid, dim3(64 * REC_WAVES), 0, stream, codes,
+                       scales, up, down, w_hat, n, k, s);
+  else if (group == 1)
+    hipLaunchKernelGGL((k_reconstruct<RANK, 1>), grid, dim3(64 * REC_WAVES), 0, stream, codes,
                        scales, up, down, w_hat, n, k, s);
   else if (group == 32)
     hipLaunchKernelGGL((k_reconstruct<RANK, 32>), grid, dim3(64 * REC_WAVES), 0, stream, codes,
