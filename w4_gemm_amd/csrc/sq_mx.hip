@@ -141,9 +141,18 @@ __global__ void __launch_bounds__(256) k_mx_transpose(const uint16_t* __restrict
 }
 
 // Grid (ceil(m/16), ceil(nblk/4)); wave w of workgroup (i, j) owns rows 16i..
-// and block 4j + w.  Writes xq [m][k/2], xs [m][k/32] and, when rank > 0, the
-// workgroup's partial t_part[j][row][r] (its four blocks summed in wave order).
-template <int RANK>
+// and block 4j + w.  Writes xq [m][k/2], the exponents and, when rank > 0,
+// the workgroup's partial t_part[j][row][r] (its four blocks summed in wave
+// order).  Exponents: PERM = false, xs [m][k/32]; PERM = true, the order in
+// which the contraction's MFMA lanes use them: for every 128-row group R and
+// 128-value stage s a 512-byte record [g][fr][i] holding the exponent of row
+// 128R + 16i + fr, block 4s + g (one 8-byte read per lane and stage).
+__device__ __forceinline__ int64_t mx_perm_exp_index(int64_t row, int64_t blk32, int64_t k) {
+  const int64_t grp = row >> 7, s = blk32 >> 2;
+  return (grp * (k >> 7) + s) * 512 + (blk32 & 3) * 128 + (row & 15) * 8 + ((row >> 4) & 7);
+}
+
+template <int RANK, bool PERM>
 __global__ void __launch_bounds__(64 * MX_PRE_WAVES) k_mx_quant_act(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ downT, uint8_t* __restrict__ xq,
     uint8_t* __restrict__ xs, float* __restrict__ t_part, int64_t m, int64_t k) {
@@ -215,7 +224,12 @@ __global__ void __launch_bounds__(64 * MX_PRE_WAVES) k_mx_quant_act(
   u32x4* dst = reinterpret_cast<u32x4*>(xq + row * (k >> 1) + (col >> 1));
   dst[0] = o0;
   dst[1] = o1;
-  *reinterpret_cast<uint16_t*>(xs + row * (k >> 5) + (col >> 5)) = (uint16_t)(e0 | (e1 << 8));
+  if constexpr (PERM) {
+    xs[mx_perm_exp_index(row, col >> 5, k)] = (uint8_t)e0;
+    xs[mx_perm_exp_index(row, (col >> 5) + 1, k)] = (uint8_t)e1;
+  } else {
+    *reinterpret_cast<uint16_t*>(xs + row * (k >> 5) + (col >> 5)) = (uint16_t)(e0 | (e1 << 8));
+  }
 }
 
 // t = sum over the slices in order, split into bf16 hi + lo (t - hi rounded).
@@ -270,11 +284,17 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
     int rank, int y_bf16) {
   constexpr int FM = 8, FN = 4;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t mt = (m + MXG_BM - 1) / MXG_BM, nt = (n + MXG_BN - 1) / MXG_BN;
   int64_t tile_m, tile_n;
   xcd_tile(blockIdx.x, mt * nt, nt, tile_m, tile_n);
+  // the tile indices come out of 64-bit divisions done on the vector unit;
+  // pin them to scalar registers so that the buffer descriptors built from
+  // them stay scalar (a descriptor in vector registers turns every load into
+  // a loop over lanes)
+  tile_m = __builtin_amdgcn_readfirstlane((int)tile_m);
+  tile_n = __builtin_amdgcn_readfirstlane((int)tile_n);
   const int64_t m0 = tile_m * MXG_BM, n0 = tile_n * MXG_BN;
   const int64_t KT = k >> 7;
   const int64_t hk = k >> 1, ek = k >> 5;   // code and exponent bytes per row
@@ -285,14 +305,20 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
       (void*)(xq + m0 * hk), (short)0, (int)(a_rows * hk), 0x00020000);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(wq + n0 * hk), (short)0, (int)(b_rows * hk), 0x00020000);
+  // activation exponents in the lane order (see k_mx_quant_act): the tile's
+  // two 128-row groups, 512 bytes per group and stage
+  const int64_t ks = k >> 7;
+  const int64_t a_groups = (m + 127) >> 7;
   const __amdgpu_buffer_rsrc_t sa_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(xs + m0 * ek), (short)0, (int)(a_rows * ek), 0x00020000);
+      (void*)xs, (short)0, (int)(a_groups * ks * 512), 0x00020000);
   const __amdgpu_buffer_rsrc_t sb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(ws + n0 * ek), (short)0, (int)(b_rows * ek), 0x00020000);
 
   // loaders: wave w fills code rows 32w .. 32w+31 of both operands (two
-  // instructions of 16 rows each) and, waves 0-3 / 4-7, exponent rows
-  // 64(w%4) .. +64 of A / B (rows past the matrix edge repeat the last row)
+  // instructions of 16 rows each); waves 0-3 each load a 256-byte quarter
+  // of the stage's 1 KB of activation exponents (group w/2, half w%2; a
+  // group past the last one reads zeros), waves 4-7 the weight exponent
+  // words of rows 64(w-4) .. +64 (rows past the matrix edge repeat the last)
   uint32_t c_off_a[2], c_off_b[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -301,9 +327,10 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
     c_off_a[i] = (uint32_t)min((int64_t)r, a_rows - 1) * (uint32_t)hk + 16u * slot;
     c_off_b[i] = (uint32_t)min((int64_t)r, b_rows - 1) * (uint32_t)hk + 16u * slot;
   }
-  const int er = 64 * (wave & 3) + lane;
   const bool exp_a = wave < 4;
-  const uint32_t e_off = (uint32_t)min((int64_t)er, (exp_a ? a_rows : b_rows) - 1) * (uint32_t)ek;
+  const uint32_t e_off =
+      exp_a ? (uint32_t)((((m0 >> 7) + (wave >> 1)) * ks) * 512 + (wave & 1) * 256 + lane * 4)
+            : (uint32_t)min((int64_t)(64 * (wave & 3) + lane), b_rows - 1) * (uint32_t)ek;
 
   auto issue = [&](int64_t kt, uint8_t* ab, uint8_t* bb, uint8_t* sab, uint8_t* sbb) {
     const int so = (int)(kt * 64);
@@ -315,15 +342,15 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
                                                c_off_b[i], so, 0, 0);
     }
     __builtin_amdgcn_raw_ptr_buffer_load_lds(exp_a ? sa_rsrc : sb_rsrc,
-                                             (mx_lds_t)((exp_a ? sab : sbb) + 64 * (wave & 3) * 4), 4,
-                                             e_off, (int)(kt * 4), 0, 0);
+                                             (mx_lds_t)((exp_a ? sab : sbb) + 256 * (wave & 3)), 4,
+                                             e_off, (int)(kt * (exp_a ? 512 : 4)), 0, 0);
   };
 
   // fragment addresses (rows 16i + fr share the swizzle of fr)
   const uint32_t swz = (uint32_t)(g ^ ((fr >> 1) & 3));
   const uint32_t a_lane = (uint32_t)(128 * wm + fr) * 64 + 16 * swz;
   const uint32_t b_lane = (uint32_t)(64 * wn + fr) * 64 + 16 * swz;
-  const uint32_t sa_lane = (uint32_t)(128 * wm + fr) * 4 + g;
+  const uint32_t sa_lane = (uint32_t)(512 * wm + 128 * g + 8 * fr);
   const uint32_t sb_lane = (uint32_t)(64 * wn + fr) * 4 + g;
 
   f32x4 acc[FM][FN];
@@ -341,20 +368,26 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
       bf[j] = (i32x8){(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
       sbv[j] = sbb[sb_lane + j * 64];
     }
+    // the eight A exponents of the lane in one read; byte i & 3 of word i / 4
+    // is selected by the instruction's scale byte select
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 sa8 = *reinterpret_cast<const u32x2*>(sab + sa_lane);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const u32x4 q = *reinterpret_cast<const u32x4*>(ab + a_lane + i * 1024);
       const i32x8 af = (i32x8){(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
-      const int sav = sab[sa_lane + i * 64];
+      const int sav = (int)sa8[i >> 2];
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 4, 4, 0,
-                                                                     sav, 0, sbv[j]);
+      for (int j = 0; j < FN; ++j) {
+        switch (i & 3) {
+          case 0: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 4, 4, 0, sav, 0, sbv[j]); break;
+          case 1: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 4, 4, 1, sav, 0, sbv[j]); break;
+          case 2: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 4, 4, 2, sav, 0, sbv[j]); break;
+          default: acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 4, 4, 3, sav, 0, sbv[j]); break;
+        }
+      }
     }
   };
-  // wait for this wave's loads of the current stage (the five of the next
-  // stage, issued later, may stay in flight: vmcnt(5)) and its LDS reads,
-  // then meet the other waves
   auto sync = [&]() {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x0F75);   // vmcnt(5)
@@ -479,7 +512,7 @@ MxPlan plan_mx(int64_t m, int64_t n, int64_t k, int rank) {
   p.slices = (int)(((k >> 8) + MX_PRE_WAVES - 1) / MX_PRE_WAVES);
   size_t off = 0;
   p.off_xq = off;     off = align256(off + (size_t)m * (k >> 1));
-  p.off_xs = off;     off = align256(off + (size_t)m * (k >> 5));
+  p.off_xs = off;     off = align256(off + (size_t)((m + 127) / 128) * 128 * (k >> 5));
   p.off_downT = off;  off = align256(off + (size_t)k * std::max(rank, 1) * 2);
   p.off_tpart = off;  off = align256(off + (size_t)p.slices * m * std::max(rank, 1) * 4);
   p.off_thi = off;    off = align256(off + (size_t)m * std::max(rank, 1) * 2);
@@ -500,7 +533,7 @@ hipError_t launch_quantize_mx(const float* w, const uint16_t* up, const uint16_t
 hipError_t launch_quantize_act_mx(const uint16_t* x, int64_t m, int64_t k, uint8_t* xq, uint8_t* xs,
                                   hipStream_t stream) {
   dim3 grid((unsigned)((m + 15) / 16), (unsigned)(((k >> 8) + MX_PRE_WAVES - 1) / MX_PRE_WAVES));
-  hipLaunchKernelGGL(k_mx_quant_act<0>, grid, dim3(64 * MX_PRE_WAVES), 0, stream, x,
+  hipLaunchKernelGGL((k_mx_quant_act<0, false>), grid, dim3(64 * MX_PRE_WAVES), 0, stream, x,
                      (const uint16_t*)nullptr, xq, xs, (float*)nullptr, m, k);
   return hipGetLastError();
 }
@@ -524,7 +557,7 @@ hipError_t launch_fwd_mx(const MxPlan& p, const uint16_t* x, const uint8_t* wq, 
   }
   const dim3 ag((unsigned)((p.m + 15) / 16), (unsigned)p.slices);
 #define SQ_MXACT(R)                                                                              \
-  hipLaunchKernelGGL(k_mx_quant_act<R>, ag, dim3(64 * MX_PRE_WAVES), 0, stream, x,              \
+  hipLaunchKernelGGL((k_mx_quant_act<R, true>), ag, dim3(64 * MX_PRE_WAVES), 0, stream, x,      \
                      (const uint16_t*)downT, xq, xs, tpart, p.m, p.k)
   if (p.rank == 0) SQ_MXACT(0);
   else if (p.rank == 16) SQ_MXACT(16);
