@@ -32,6 +32,12 @@ per row) and the MXFP4 mode (rank 32, E2M1 codes with E8M0 block-32
 exponents, FP4 x FP4 forward on the scaled MFMA, against the 10.1 PFLOP/s
 dense FP4 peak) at the same shape: forward, reconstruct and quantizer.
 
+Context fields: torch's bf16 GEMM (hipBLASLt) on the same activations and the
+dense bf16 weight (a comparator only, the on-box counterpart of the pages'
+production bf16 GEMM), the oracle's quantizer sweep and reconstruct on a few
+sampled weight rows beside its forward, and the current shader and memory
+clock levels.
+
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 4]
        python bench.py --ops copy      (the counter calibration copy only)
 """
@@ -91,8 +97,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
-    ap.add_argument("--ops", default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs,w8,mx")
+    ap.add_argument("--cpu-rows", type=int, default=4480)
+    ap.add_argument("--ops",
+                    default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs,w8,mx,bf16gemm")
     ap.add_argument("--small-m", default="1,16,128")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -216,6 +223,9 @@ def main():
     # ---------------------------------------------------------------- MXFP4 mode
     if "mx" in ops:
         res["mx"] = mx_run(torch, W, dev, w, x, up, down, what, M, N, K, args.steps, args.warmup)
+    # ---------------------------------------------------------------- comparator
+    if "bf16gemm" in ops:
+        res["bf16gemm"] = bf16_gemm_run(torch, dev, w, x, M, N, K, args.steps, args.warmup)
     # ---------------------------------------------------------------- streaming builder
     if "builder" in ops:
         res["builder"] = builder_run(torch, dev)
@@ -286,6 +296,8 @@ def main():
         out["w8"] = res["w8"]
     if "mx" in res:
         out["mx"] = res["mx"]
+    if "bf16gemm" in res:
+        out["bf16_gemm_hipblaslt"] = res["bf16gemm"]
     if "smallm" in res:
         out["fwd_small_m"] = res["smallm"]
     if "configs" in res:
@@ -313,9 +325,11 @@ def main():
     line["timed_wall_s"] = wall
     line["setup_s"] = t_setup
     line["device"] = torch.cuda.get_device_name(0)
+    line["clocks"] = read_clocks()
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p0, x, cfg, args.cpu_rows)
+        line["cpu_baseline_other"] = cpu_other(p0, w, cfg)
     print(json.dumps(line), flush=True)
     return 0
 
@@ -562,6 +576,72 @@ def small_m_sweep(torch, W, dev, ms, steps, warmup):
                        "pct_hbm_peak": 100.0 * by / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                        "tflops": (2.0 * m * N * K + 2.0 * m * R * (N + K)) / (t * 1e-3) / 1e12}
     return out
+
+
+def bf16_gemm_run(torch, dev, w, x, M, N, K, steps, warmup):
+    """Comparator only (not a code path): torch's bf16 GEMM (hipBLASLt) of the
+    same activations with the dense bf16 weight, y = x @ W^T, at the same
+    shape; the on-box counterpart of the pages' production bf16 GEMM column."""
+    wt = w.t().contiguous().to(torch.bfloat16)   # [K, N], no transposed view
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        torch.mm(x, wt, out=y)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record()
+        torch.mm(x, wt, out=y)
+        b.record()
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    del wt, y
+    torch.cuda.empty_cache()
+    return {"ms": t, "tflops": 2.0 * M * N * K / (t * 1e-3) / 1e12}
+
+
+def read_clocks():
+    """Current shader and memory clock levels as the driver lists them (best effort)."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device"))[:1]:
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [l.strip() for l in f if l.strip().endswith("*")]
+                out[name] = cur[0] if cur else None
+            except OSError:
+                out[name] = None
+    return out
+
+
+def cpu_other(p, w, cfg, rows=1024):
+    """The oracle's quantizer (the 31-fraction sweep of the rotated residual,
+    without the SVD) and reconstruct on `rows` sampled weight rows."""
+    import oracle as O
+    sel = np.sort(np.random.default_rng(2).choice(cfg.N, rows, replace=False))
+    wr = w[sel].cpu().numpy().astype(np.float64)
+    up = p.up.float().cpu().numpy().astype(np.float64)
+    dn = p.down.float().cpu().numpy().astype(np.float64)
+    r = O.residual(wr, up[sel], dn)
+    t = time.perf_counter()
+    res = O.quantize_residual(r, cfg.group)
+    t_q = time.perf_counter() - t
+    codes = p.codes[torch_index(sel, p.codes)].cpu().numpy()
+    scales = p.scales[torch_index(sel, p.scales)].cpu().numpy()
+    t = time.perf_counter()
+    wh = O.reconstruct(O.unpack(codes), O.fp16_decode(scales), up[sel], dn, cfg.group)
+    t_r = time.perf_counter() - t
+    assert np.all(np.isfinite(wh)) and res.q.shape == (rows, cfg.K)
+    elems = rows * cfg.K
+    return {"quantize_sweep": {"value": elems / t_q / 1e6, "unit": "Melem/s", "seconds": t_q,
+                               "sample": f"oracle.quantize_residual on {rows} of {cfg.N} rows, K={cfg.K}"},
+            "reconstruct": {"value": elems / t_r / 1e6, "unit": "Melem/s", "seconds": t_r,
+                            "sample": f"oracle.reconstruct on {rows} of {cfg.N} rows, K={cfg.K}"}}
+
+
+def torch_index(sel, t):
+    import torch
+    return torch.from_numpy(sel).to(t.device)
 
 
 def cpu_baseline(p, x, cfg, rows):
