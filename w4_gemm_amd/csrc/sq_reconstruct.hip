@@ -204,8 +204,15 @@ __global__ void __launch_bounds__(64 * REC_WAVES) k_reconstruct(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nblk = k >> 8;
   const int64_t nstr = (n + 15) / 16;
-  const int64_t blk = blockIdx.x % nblk;
-  const int64_t first = (int64_t)(blockIdx.x / nblk) * REC_WAVES * strips + wave;
+  // Workgroup ids congruent mod 8 run on the same XCD (L2).  Give each XCD a
+  // contiguous run of (strip run, block) pairs, so that the neighbouring
+  // blocks of a row, whose scales share 128-byte lines, are read through one
+  // L2 instead of up to eight.
+  const int64_t nwg = (int64_t)gridDim.x, lin = blockIdx.x;
+  const int64_t xcd = lin & 7, per = nwg >> 3, rem = nwg & 7;
+  const int64_t t = xcd * per + min(xcd, rem) + (lin >> 3);
+  const int64_t blk = t % nblk;
+  const int64_t first = (t / nblk) * REC_WAVES * strips + wave;
   const int c = lane & 15, g = lane >> 4;
 
   // Column of MFMA output row rho in accumulator register 4t + rho%4: the
