@@ -170,14 +170,15 @@ def test_fwd_ragged_and_rank0():
 
 
 def test_fwd_small_m_tiles():
-    # the small-M contraction with one, two and four 16-row tiles, K slices
-    # that are and are not whole multiples of its prefetch step, ragged N
+    # the small-M contraction with one, two and four 16-row tiles and, above
+    # 64 rows, two 64-row chunks (the second ragged); K slices that are and
+    # are not whole multiples of its prefetch step; ragged N
     rng = np.random.default_rng(11)
     from synth import gen_activations
     for k in (1280, 2048):
         codes, scales, upb, dnb = gen_payload(rng, 200, k, 32, 32)
-        xbits = gen_activations(rng, 64, k, 0.01)
-        for m in (1, 17, 32, 33, 64):
+        xbits = gen_activations(rng, 128, k, 0.01)
+        for m in (1, 17, 32, 33, 64, 65, 100, 128):
             _fwd_checks(xbits[:m], codes, scales, upb, dnb, 32, tag=f"m{m} n200 k{k}")
 
 

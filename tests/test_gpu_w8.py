@@ -196,8 +196,8 @@ def test_w8_fwd_small_m():
         q, scales, upb, dnb = gen_payload_w8(rng, n, k, max(rank, 1))
         if rank == 0:
             upb = dnb = None
-        xbits = gen_activations(rng, 64, k, 0.01)
-        for m in (1, 5, 17, 33, 64):
+        xbits = gen_activations(rng, 128, k, 0.01)
+        for m in (1, 5, 17, 33, 64, 65, 128):
             _fwd_checks(xbits[:m], q, scales, upb, dnb, tag=f"m{m} n{n} k{k} r{rank}")
 
 
