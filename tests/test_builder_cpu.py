@@ -136,3 +136,41 @@ def test_kill_and_resume_is_byte_identical(src, tmp_path, victim):
     final = build(path, out, after_write=seen.append)
     assert set(seen).isdisjoint(done_before) and victim in seen     # only the rest is redone
     assert open(final, "rb").read() == open(ref, "rb").read()
+
+
+def oracle_quantize_w8(w, up_bits, dn_bits, group):
+    dec = lambda b: (np.zeros((w.shape[0] if b is up_bits else w.shape[1], 0)) if b is None
+                     else O.bf16_decode(b))
+    res = O.quantize_weight_w8(np.asarray(w, np.float64), dec(up_bits), dec(dn_bits))
+    return res.q.astype(np.int8), res.scale.astype(np.float16).view(np.uint16), res.fidx
+
+
+def oracle_quantize_mx(w, up_bits, dn_bits, group):
+    dec = lambda b: (np.zeros((w.shape[0] if b is up_bits else w.shape[1], 0)) if b is None
+                     else O.bf16_decode(b))
+    codes, exps = O.quantize_weight_mx(np.asarray(w, np.float64), dec(up_bits), dec(dn_bits))
+    return O.mx_pack(codes), exps
+
+
+@pytest.mark.parametrize("fmt,rank", [("int8", 16), ("mxfp4", 32)])
+def test_build_other_codecs(src, tmp_path, fmt, rank):
+    path, t = src
+    q = oracle_quantize_w8 if fmt == "int8" else oracle_quantize_mx
+    out = B.build(path, str(tmp_path / fmt), rank=rank, group=32, svd="exact", quantize=q,
+                  lowrank=oracle_lowrank, fmt=fmt)
+    from safetensors import safe_open
+    with safe_open(out, framework="pt") as f:
+        assert f.metadata()["codec"] == fmt
+        assert torch.equal(f.get_tensor("embed.weight"), t["embed.weight"])
+        for name in ("blocks.0.attn.q.weight", "blocks.1.mlp.down.weight"):
+            w = t[name].float().numpy()
+            up_b, dn_b = oracle_lowrank(w, rank, name)
+            arrays = q(w, up_b, dn_b, 32)
+            names = ("codes", "scales", "fidx") if fmt == "int8" else ("codes", "exps")
+            for s, a in zip(names, arrays):
+                got = f.get_tensor(f"{name}.{s}")
+                got = got.view(torch.int16).numpy().view(np.uint16) if got.dtype == torch.float16 else got.numpy()
+                assert np.array_equal(got, a), (name, s)
+            assert f.get_tensor(f"{name}.lora_up").shape == (w.shape[0], rank)
+    with pytest.raises(ValueError):
+        B.build(path, str(tmp_path / "bad"), rank=16, group=32, fmt="w4")

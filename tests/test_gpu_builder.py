@@ -60,3 +60,36 @@ def test_builder_matches_entry_point_and_resumes(tmp_path):
         B.build(src, str(tmp_path / "s2"), rank=32, group=32, after_write=stop)
     out2 = B.build(src, str(tmp_path / "s2"), rank=32, group=32)
     assert open(out2, "rb").read() == open(out, "rb").read()
+
+
+@pytest.mark.parametrize("fmt,rank", [("int8", 16), ("mxfp4", 32)])
+def test_builder_other_codecs_match_entry_points(tmp_path, fmt, rank):
+    import w4_gemm_amd as W
+    from safetensors import safe_open
+    from w4_gemm_amd import builder as B
+    src = str(tmp_path / "m.safetensors")
+    t = _source(src)
+    out = B.build(src, str(tmp_path / fmt), rank=rank, group=32, fmt=fmt)
+    d = torch.device("cuda")
+    with safe_open(out, framework="pt") as f:
+        assert f.metadata()["codec"] == fmt
+        for name in ("a.weight", "b.weight"):
+            w = t[name].float().to(d)
+            up, dn = f.get_tensor(f"{name}.lora_up").to(d), f.get_tensor(f"{name}.lora_down").to(d)
+            if fmt == "int8":
+                p, fidx, flags = W.quantize_weight_w8(w, up, dn)
+                torch.cuda.synchronize()
+                assert torch.equal(p.codes.cpu(), f.get_tensor(f"{name}.codes"))
+                assert torch.equal(p.scales.cpu().view(torch.int16), f.get_tensor(f"{name}.scales").view(torch.int16))
+                assert torch.equal(fidx.cpu(), f.get_tensor(f"{name}.fidx"))
+                what = W.reconstruct_bf16_w8(p).float()
+            else:
+                p, flags = W.quantize_weight_mx4(w, up, dn)
+                torch.cuda.synchronize()
+                assert torch.equal(p.codes.cpu(), f.get_tensor(f"{name}.codes"))
+                assert torch.equal(p.exps.cpu(), f.get_tensor(f"{name}.exps"))
+                what = W.reconstruct_bf16_mx4(p).float()
+            assert int(flags[0]) == 0
+            e = float((what - w).norm() / w.norm())
+            print(f"{fmt} {name}: relF(W_hat, W) = {e:.4f}")
+            assert e < 0.15

@@ -9,13 +9,17 @@ GPU for large weights), then sq_quantize_weight on the GPU.
 
 Plan (a pure function of the source header and the options):
   source tensors in name order; a 2-D floating tensor [N, K] with K % 256 == 0
-  whose name matches `include` becomes
+  whose name matches `include` becomes, with the default W4 codec,
       <name>.codes      U8    [N, K/2]
       <name>.scales     F16   [N, K/group]
       <name>.fidx       U8    [N, K/group]   (chosen fraction index)
       <name>.lora_up    BF16  [N, rank]      (rank > 0)
       <name>.lora_down  BF16  [K, rank]      (rank > 0)
-  and every other tensor is copied byte for byte.  The output is a
+  and every other tensor is copied byte for byte.  The other codecs of the
+  library (the page's v3.1 int8-residual mode and the FP4 alternative of its
+  "Residual codecs" bullet, as MXFP4) replace the first three by
+      int8:  <name>.codes I8 [N, K], <name>.scales F16 [N], <name>.fidx U8 [N]
+      mxfp4: <name>.codes U8 [N, K/2] (E2M1 nibbles), <name>.exps U8 [N, K/32]  The output is a
   safetensors file: header (padded with spaces to a multiple of 8 bytes),
   then the data regions in plan order, contiguous.
 
@@ -35,7 +39,8 @@ an uninterrupted one.  Peak host memory is about one source tensor and its
 outputs.
 
 Usage: python -m w4_gemm_amd.builder --src model.safetensors --out-dir slab \
-           [--rank 32] [--group 32] [--svd auto|exact|randomized] [--include REGEX]
+           [--format w4|int8|mxfp4] [--rank 32] [--group 32] [--svd auto|exact|randomized]
+           [--include REGEX]
 """
 from __future__ import annotations
 
@@ -105,7 +110,23 @@ class Plan:
     digest: str
 
 
-def make_plan(src: str, rank: int, group: int, svd: str, include: str) -> Plan:
+CODECS = ("w4", "int8", "mxfp4")
+
+
+def codec_outputs(fmt: str, name: str, n: int, k: int, group: int):
+    """The quantizer's output tensors of one weight, in file order."""
+    if fmt == "int8":
+        return [OutTensor(f"{name}.codes", "I8", (n, k)), OutTensor(f"{name}.scales", "F16", (n,)),
+                OutTensor(f"{name}.fidx", "U8", (n,))]
+    if fmt == "mxfp4":
+        return [OutTensor(f"{name}.codes", "U8", (n, k // 2)),
+                OutTensor(f"{name}.exps", "U8", (n, k // 32))]
+    return [OutTensor(f"{name}.codes", "U8", (n, k // 2)),
+            OutTensor(f"{name}.scales", "F16", (n, k // group)),
+            OutTensor(f"{name}.fidx", "U8", (n, k // group))]
+
+
+def make_plan(src: str, rank: int, group: int, svd: str, include: str, fmt: str = "w4") -> Plan:
     hdr, meta, _ = read_header(src)
     pat = re.compile(include)
     units = []
@@ -117,9 +138,7 @@ def make_plan(src: str, rank: int, group: int, svd: str, include: str) -> Plan:
         u = Unit(name, "w4" if quant else "copy", dt, shape, rng)
         if quant:
             n, k = shape
-            u.outs = [OutTensor(f"{name}.codes", "U8", (n, k // 2)),
-                      OutTensor(f"{name}.scales", "F16", (n, k // group)),
-                      OutTensor(f"{name}.fidx", "U8", (n, k // group))]
+            u.outs = codec_outputs(fmt, name, n, k, group)
             if rank > 0:
                 u.outs += [OutTensor(f"{name}.lora_up", "BF16", (n, rank)),
                            OutTensor(f"{name}.lora_down", "BF16", (k, rank))]
@@ -129,6 +148,8 @@ def make_plan(src: str, rank: int, group: int, svd: str, include: str) -> Plan:
     off = 0
     entries = {"__metadata__": {"format": FORMAT, "rank": str(rank), "group": str(group),
                                 "svd": svd, "include": include}}
+    if fmt != "w4":
+        entries["__metadata__"]["codec"] = fmt
     for u in units:
         for o in u.outs:
             o.offset = off
@@ -210,6 +231,41 @@ def gpu_quantize(w: np.ndarray, up_bits, dn_bits, group: int):
             fidx.cpu().numpy())
 
 
+def gpu_quantize_w8(w: np.ndarray, up_bits, dn_bits, group: int):
+    """sq_quantize_weight_w8 on the GPU: (codes i8, scale bits u16 [N], fidx u8 [N])."""
+    import torch
+    from . import api
+    d = torch.device("cuda")
+    bf = (lambda b: None if b is None else
+          torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(d))
+    p, fidx, flags = api.quantize_weight_w8(torch.from_numpy(np.ascontiguousarray(w)).to(d),
+                                            bf(up_bits), bf(dn_bits))
+    torch.cuda.synchronize()
+    f = int(flags[0])
+    if f:
+        raise FloatingPointError(f"quantizer flags {f:#x} (1 non-finite weight, 2 fp16 scale overflow)")
+    return (p.codes.cpu().numpy(), p.scales.view(torch.int16).cpu().numpy().view(np.uint16),
+            fidx.cpu().numpy())
+
+
+def gpu_quantize_mx(w: np.ndarray, up_bits, dn_bits, group: int):
+    """sq_quantize_weight_mx4 on the GPU: (codes u8 [N, K/2], exps u8 [N, K/32])."""
+    import torch
+    from . import api
+    d = torch.device("cuda")
+    bf = (lambda b: None if b is None else
+          torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(d))
+    p, flags = api.quantize_weight_mx4(torch.from_numpy(np.ascontiguousarray(w)).to(d),
+                                       bf(up_bits), bf(dn_bits))
+    torch.cuda.synchronize()
+    if int(flags[0]):
+        raise FloatingPointError(f"quantizer flags {int(flags[0]):#x} (1 non-finite residual)")
+    return p.codes.cpu().numpy(), p.exps.cpu().numpy()
+
+
+GPU_QUANTIZE = {"w4": gpu_quantize, "int8": gpu_quantize_w8, "mxfp4": gpu_quantize_mx}
+
+
 # ---------------------------------------------------------------- the build
 def _write_state(out_dir: str, state: dict):
     tmp = os.path.join(out_dir, STATE + ".tmp")
@@ -226,22 +282,27 @@ def _write_state(out_dir: str, state: dict):
 
 
 def build(src: str, out_dir: str, rank: int = 32, group: int = 32, svd: str = "auto",
-          include: str = ".*", quantize=None, lowrank=None, after_write=None, log=None) -> str:
+          include: str = ".*", quantize=None, lowrank=None, after_write=None, log=None,
+          fmt: str = "w4") -> str:
     """Build (or resume) the slab; returns the path of the finished file.
 
-    quantize(w_f32, up_bits, down_bits, group) -> (codes, scale_bits, fidx) and
-    lowrank(w_f32, rank, name) -> (up_bits, down_bits) default to the GPU
-    steps above.  after_write(unit_name) is called once a tensor's first output
-    is written and before the rest (a hook for interruption tests).
+    quantize(w_f32, up_bits, down_bits, group) -> the codec's arrays in file
+    order (W4: codes, scale_bits, fidx) and lowrank(w_f32, rank, name) ->
+    (up_bits, down_bits) default to the GPU steps above.  after_write(unit_name)
+    is called once a tensor's first output is written and before the rest (a
+    hook for interruption tests).
     """
-    if group not in (32, 64) or rank not in (0, 32, 64):
-        raise ValueError("group must be 32 or 64 and rank 0, 32 or 64")
+    if fmt not in CODECS:
+        raise ValueError(f"format must be one of {CODECS}")
+    ranks = (0, 32, 64) if fmt == "w4" else (0, 16, 32, 64)
+    if group not in (32, 64) or rank not in ranks:
+        raise ValueError(f"group must be 32 or 64 and rank one of {ranks}")
     if svd not in ("auto", "exact", "randomized"):
         raise ValueError("svd must be auto, exact or randomized")
-    quantize = quantize or gpu_quantize
+    quantize = quantize or GPU_QUANTIZE[fmt]
     lowrank = lowrank or (lambda w, r, name: gpu_lowrank(w, r, name, svd))
     os.makedirs(out_dir, exist_ok=True)
-    plan = make_plan(src, rank, group, svd, include)
+    plan = make_plan(src, rank, group, svd, include, fmt)
     final, partial = os.path.join(out_dir, SLAB), os.path.join(out_dir, PARTIAL)
     spath = os.path.join(out_dir, STATE)
     state = None
@@ -277,10 +338,7 @@ def build(src: str, out_dir: str, rank: int = 32, group: int = 32, svd: str = "a
                     up = dn = None
                     if rank > 0:
                         up, dn = lowrank(w, rank, u.src)
-                    codes, scale_bits, fidx = quantize(w, up, dn, group)
-                    blobs = [np.ascontiguousarray(codes, np.uint8).tobytes(),
-                             np.ascontiguousarray(scale_bits, np.uint16).tobytes(),
-                             np.ascontiguousarray(fidx, np.uint8).tobytes()]
+                    blobs = [np.ascontiguousarray(a).tobytes() for a in quantize(w, up, dn, group)]
                     if rank > 0:
                         blobs += [np.ascontiguousarray(up, np.uint16).tobytes(),
                                   np.ascontiguousarray(dn, np.uint16).tobytes()]
@@ -315,9 +373,10 @@ def main(argv=None) -> int:
     ap.add_argument("--group", type=int, default=32)
     ap.add_argument("--svd", default="auto", choices=("auto", "exact", "randomized"))
     ap.add_argument("--include", default=".*")
+    ap.add_argument("--format", default="w4", choices=CODECS)
     a = ap.parse_args(argv)
     path = build(a.src, a.out_dir, a.rank, a.group, a.svd, a.include,
-                 log=lambda s: print(s, flush=True))
+                 log=lambda s: print(s, flush=True), fmt=a.format)
     print(path)
     return 0
 
