@@ -194,6 +194,16 @@ def test_mx_fwd_shapes():
         _fwd_checks(xbits, codes, exps, upb, dnb, tag=f"m{m} n{n} k{k} r{rank}")
 
 
+def test_mx_fwd_split_k():
+    # grids of fewer than 128 tiles split K: 4 tiles x 8 splits of 8 stages,
+    # 3 tiles x 3 splits of 8, 9 and 9 stages, 2 tiles x 5 splits of 9 or 10
+    rng = np.random.default_rng(37)
+    for (m, n, k, rank) in [(3, 1000, 8192, 32), (40, 513, 3328, 16), (256, 257, 5888, 64)]:
+        codes, exps, upb, dnb = gen_payload_mx(rng, n, k, rank)
+        xbits = gen_activations(rng, m, k, 0.01)
+        _fwd_checks(xbits, codes, exps, upb, dnb, tag=f"split-K m{m} n{n} k{k} r{rank}")
+
+
 def test_mx_end_to_end_quantized_layer():
     # device quantizer -> device forward; the FP4 layer tracks the exact layer
     import w4_gemm_amd as W

@@ -28,7 +28,8 @@ struct MxPlan {
   int64_t m, n, k;
   int rank;
   int slices;   // workgroups along K of the activation pass (4 blocks each)
-  size_t off_xq, off_xs, off_downT, off_tpart, off_thi, off_tlo, total;
+  int splits;   // split-K factor of the FP4 contraction
+  size_t off_xq, off_xs, off_downT, off_tpart, off_thi, off_tlo, off_part, total;
 };
 MxPlan plan_mx(int64_t m, int64_t n, int64_t k, int rank);
 hipError_t launch_quantize_mx(const float* w, const uint16_t* up, const uint16_t* down,

@@ -239,8 +239,17 @@ __global__ void __launch_bounds__(256) k_mx_tsum(const float* __restrict__ t_par
                                                   int slices) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= m * rank) return;
+  // fixed summation order; the loads of a group of eight are all in flight
   float t = 0.0f;
-  for (int q = 0; q < slices; ++q) t += t_part[(int64_t)q * m * rank + i];
+  int q = 0;
+  for (; q + 8 <= slices; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = t_part[(int64_t)(q + u) * m * rank + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t += v[u];
+  }
+  for (; q < slices; ++q) t += t_part[(int64_t)q * m * rank + i];
   const uint16_t hb = f32_to_bf16(t);
   thi[i] = hb;
   tlo[i] = f32_to_bf16(t - bf16_to_f32(hb));
@@ -276,19 +285,25 @@ __shared__ __attribute__((aligned(16))) uint8_t mx_sb2[MXG_EXP_BYTES];
 typedef __attribute__((address_space(3))) void* mx_lds_t;
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
+// SKIP (grids with a single ragged tile row): a wave leaves out the MFMAs of
+// 16-row fragments that lie wholly past row m.
+template <bool SKIP>
 __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint16_t* __restrict__ thi, const uint16_t* __restrict__ tlo,
     const uint16_t* __restrict__ up, void* __restrict__ y, int64_t m, int64_t n, int64_t k,
-    int rank, int y_bf16) {
+    int rank, int y_bf16, int splits, float* __restrict__ partial) {
   constexpr int FM = 8, FN = 4;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int64_t mt = (m + MXG_BM - 1) / MXG_BM, nt = (n + MXG_BN - 1) / MXG_BN;
+  // workgroup b: split b / tiles of tile b % tiles
+  const uint32_t tiles = (uint32_t)(mt * nt);
+  const int split = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / tiles));
   int64_t tile_m, tile_n;
-  xcd_tile(blockIdx.x, mt * nt, nt, tile_m, tile_n);
+  xcd_tile(blockIdx.x - (uint32_t)split * tiles, tiles, nt, tile_m, tile_n);
   // the tile indices come out of 64-bit divisions done on the vector unit;
   // pin them to scalar registers so that the buffer descriptors built from
   // them stay scalar (a descriptor in vector registers turns every load into
@@ -296,7 +311,11 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
   tile_m = __builtin_amdgcn_readfirstlane((int)tile_m);
   tile_n = __builtin_amdgcn_readfirstlane((int)tile_n);
   const int64_t m0 = tile_m * MXG_BM, n0 = tile_n * MXG_BN;
-  const int64_t KT = k >> 7;
+  // this split's stages kb .. kb + KT - 1 (128 K values each)
+  const int64_t kall = k >> 7;
+  const int64_t kb = __builtin_amdgcn_readfirstlane((int)((int64_t)split * kall / splits));
+  const int64_t KT =
+      __builtin_amdgcn_readfirstlane((int)(((int64_t)split + 1) * kall / splits)) - kb;
   const int64_t hk = k >> 1, ek = k >> 5;   // code and exponent bytes per row
   const int fr = lane & 15, g = lane >> 4;
 
@@ -332,7 +351,8 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
       exp_a ? (uint32_t)((((m0 >> 7) + (wave >> 1)) * ks) * 512 + (wave & 1) * 256 + lane * 4)
             : (uint32_t)min((int64_t)(64 * (wave & 3) + lane), b_rows - 1) * (uint32_t)ek;
 
-  auto issue = [&](int64_t kt, uint8_t* ab, uint8_t* bb, uint8_t* sab, uint8_t* sbb) {
+  auto issue = [&](int64_t kl, uint8_t* ab, uint8_t* bb, uint8_t* sab, uint8_t* sbb) {
+    const int64_t kt = kb + kl;
     const int so = (int)(kt * 64);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -359,6 +379,7 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+  const int64_t mleft = m - (m0 + 128 * wm);   // live rows of the wave's 128
   auto compute = [&](const uint8_t* ab, const uint8_t* bb, const uint8_t* sab, const uint8_t* sbb) {
     i32x8 bf[FN];
     int sbv[FN];
@@ -374,6 +395,7 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
     const u32x2 sa8 = *reinterpret_cast<const u32x2*>(sab + sa_lane);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if (SKIP && 16 * i >= mleft) break;
       const u32x4 q = *reinterpret_cast<const u32x4*>(ab + a_lane + i * 1024);
       const i32x8 af = (i32x8){(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
       const int sav = (int)sa8[i >> 2];
@@ -421,7 +443,13 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
 
   const int64_t rbase = m0 + 128 * wm, cbase = n0 + 64 * wn;
   // rank-r branch: (t_hi + t_lo) @ up^T on bf16 MFMA (rank 16: the upper half
-  // of the 32-wide step reads zeros)
+  // of the 32-wide step reads zeros); with split-K split 0 adds it and every
+  // split stores its fp32 partial sums to partial [splits][m][n]
+  if (splits > 1) {
+    if (split > 0) rank = 0;
+    y = partial + (int64_t)split * m * n;
+    y_bf16 = 0;
+  }
   for (int rr = 0; rr < rank; rr += 32) {
     const bool rk = rr + 8 * g < rank;
 #pragma unroll
@@ -503,13 +531,47 @@ __global__ void __launch_bounds__(MXG_THREADS, 1) k_mx_gemm(
     }
 }
 
+// Split-K sum: y = sum over the splits of partial [splits][m][n], in split
+// order.
+__global__ void __launch_bounds__(256) k_mx_splitsum(const float* __restrict__ partial,
+                                                      void* __restrict__ y, int64_t mn,
+                                                      int splits, int y_bf16) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  float s = 0.0f;
+  int z = 0;
+  for (; z + 8 <= splits; z += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = partial[(int64_t)(z + u) * mn + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; z < splits; ++z) s += partial[(int64_t)z * mn + i];
+  if (y_bf16)
+    reinterpret_cast<uint16_t*>(y)[i] = f32_to_bf16(s);
+  else
+    reinterpret_cast<float*>(y)[i] = s;
+}
+
 // ---------------------------------------------------------------- host side
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Split-K factor of the FP4 contraction: one 256 x 256 tile per CU at a time,
+// so a grid of fewer than half the chip's 256 CUs splits K into as many
+// slices as fill it, each at least 8 stages (1024 K values) long.
+static int mx_splits(int64_t m, int64_t n, int64_t k) {
+  const int64_t tiles = ((m + MXG_BM - 1) / MXG_BM) * ((n + MXG_BN - 1) / MXG_BN);
+  if (tiles >= 128) return 1;
+  const int64_t s = std::min<int64_t>(256 / tiles, (k >> 7) / 8);
+  return (int)std::max<int64_t>(s, 1);
+}
 
 MxPlan plan_mx(int64_t m, int64_t n, int64_t k, int rank) {
   MxPlan p{};
   p.m = m; p.n = n; p.k = k; p.rank = rank;
   p.slices = (int)(((k >> 8) + MX_PRE_WAVES - 1) / MX_PRE_WAVES);
+  p.splits = mx_splits(m, n, k);
   size_t off = 0;
   p.off_xq = off;     off = align256(off + (size_t)m * (k >> 1));
   p.off_xs = off;     off = align256(off + (size_t)((m + 127) / 128) * 128 * (k >> 5));
@@ -517,6 +579,7 @@ MxPlan plan_mx(int64_t m, int64_t n, int64_t k, int rank) {
   p.off_tpart = off;  off = align256(off + (size_t)p.slices * m * std::max(rank, 1) * 4);
   p.off_thi = off;    off = align256(off + (size_t)m * std::max(rank, 1) * 2);
   p.off_tlo = off;    off = align256(off + (size_t)m * std::max(rank, 1) * 2);
+  p.off_part = off;   off = align256(off + (p.splits > 1 ? (size_t)p.splits * m * n * 4 : 0));
   p.total = off;
   return p;
 }
@@ -548,6 +611,7 @@ hipError_t launch_fwd_mx(const MxPlan& p, const uint16_t* x, const uint8_t* wq, 
   float* tpart = reinterpret_cast<float*>(base + p.off_tpart);
   uint16_t* thi = reinterpret_cast<uint16_t*>(base + p.off_thi);
   uint16_t* tlo = reinterpret_cast<uint16_t*>(base + p.off_tlo);
+  float* part = reinterpret_cast<float*>(base + p.off_part);
   hipError_t err;
   if (p.rank > 0) {
     const int64_t cnt = p.k * p.rank;
@@ -572,9 +636,22 @@ hipError_t launch_fwd_mx(const MxPlan& p, const uint16_t* x, const uint8_t* wq, 
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int64_t tiles = ((p.m + MXG_BM - 1) / MXG_BM) * ((p.n + MXG_BN - 1) / MXG_BN);
-  hipLaunchKernelGGL(k_mx_gemm, dim3((unsigned)tiles), dim3(MXG_THREADS), 0, stream, xq, xs, wq,
-                     wsc, thi, tlo, up, y, p.m, p.n, p.k, p.rank, y_bf16);
-  return hipGetLastError();
+  if (p.m < MXG_BM)
+    hipLaunchKernelGGL(k_mx_gemm<true>, dim3((unsigned)(tiles * p.splits)), dim3(MXG_THREADS), 0,
+                       stream, xq, xs, wq, wsc, thi, tlo, up, y, p.m, p.n, p.k, p.rank, y_bf16,
+                       p.splits, part);
+  else
+    hipLaunchKernelGGL(k_mx_gemm<false>, dim3((unsigned)(tiles * p.splits)), dim3(MXG_THREADS), 0,
+                       stream, xq, xs, wq, wsc, thi, tlo, up, y, p.m, p.n, p.k, p.rank, y_bf16,
+                       p.splits, part);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (p.splits > 1) {
+    const int64_t mn = p.m * p.n;
+    hipLaunchKernelGGL(k_mx_splitsum, dim3((unsigned)((mn + 255) / 256)), dim3(256), 0, stream,
+                       part, y, mn, p.splits, y_bf16);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 // The reconstruct runs in the strip kernel of the W4 payload (group code 1):
