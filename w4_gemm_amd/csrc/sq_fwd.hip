@@ -887,10 +887,8 @@ __global__ void __launch_bounds__(256) k_fwd_reduce(const float* __restrict__ pa
 // ---------------------------------------------------------------- host side
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Tile choice: M <= 64 the small-M kernel; the big kernel when its grid has
-// at least half a tile per CU (with the tile height, 256 or 224, that needs
-// the fewest rows-times-rounds on the chip's 256 CUs); else 128 x 128 with
-// split-K.
+// Tile choice: M <= 64 the small-M kernel; else the 256-column-tile kernel
+// with the tile height and split-K factor of least estimated time.
 FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   FwdPlan p{};
   p.m = m; p.n = n; p.k = k; p.group = group; p.rank = rank;
@@ -915,19 +913,23 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
     p.tile_m = 16 * p.skinny_mt; p.tile_n = SK_ROWS;
   } else {
     // The 256-column-tile kernel with tile height BM in {256, 224, 128} and
-    // s K splits (whole super-stages each).  Estimated time: tile-rounds of
-    // the 256 CUs times BM x stages per split (about 7.8 ns per row-stage
-    // per resident tile, measured), plus writing and re-reading the fp32
-    // partials at ~5 TB/s when s > 1.
+    // s K splits (whole super-stages each).  Estimated time: rounds of the
+    // 256 CUs (one tile each) times the stages per split times the time of
+    // one 64-deep stage of a BM-row tile, 0.71 + 0.00273 BM us (a fit to
+    // M = 96 .. 2048 on a 6144 x 16384 weight: a 128-row tile costs three
+    // quarters of a 256-row one, not half), 10 % more with the chip full;
+    // plus writing and re-reading the fp32 partials (~3.3 TB/s) and the
+    // reduce launch when s > 1.
     const int64_t nt_big = (n + BIG_BN - 1) / BIG_BN;
     double best = -1.0;
     for (int bm : {256, 224, 128}) {
       const int64_t tiles = ((m + bm - 1) / bm) * nt_big;
       for (int64_t sp = 1; sp <= 16; sp *= 2) {
         if ((KT / 4) % sp) continue;   // every split a whole number of super-stages
-        const int64_t rounds = (tiles * sp + 255) / 256;
-        double t = rounds * (double)bm * (double)(KT / sp) * 7.8e-9;
-        if (sp > 1) t += 8.0 * sp * (double)m * n / 5e12 + 3e-6;
+        const int64_t wgs = tiles * sp, rounds = (wgs + 255) / 256;
+        double t = rounds * (double)(KT / sp) * (0.71e-6 + 2.73e-9 * bm) *
+                   (1.0 + 0.1 * (double)std::min<int64_t>(wgs, 256) / 256.0);
+        if (sp > 1) t += 1.5 * 8.0 * sp * (double)m * n / 5e12 + 10e-6;
         if (best < 0.0 || t < best - 1e-9) { best = t; p.tile_m = bm; p.splits = (int)sp; }
       }
     }
