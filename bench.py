@@ -380,6 +380,10 @@ def w8_run(torch, W, dev, w, x, what, M, N, K, steps, warmup):
            "quantize_ms": t_q}
     out["fwd_pct_bf16_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_F16_TFLOPS
     out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
+    out["fwd_small_m"] = small_m_modes(
+        torch, dev, x, N, K, pay, steps, warmup,
+        lambda m: W.fwd_w8_workspace_bytes(m, p0),
+        lambda xx, yy, wss: W.linear_fwd_w8(xx, p0, out=yy, workspace=wss))
     del pays, p0, qws, ws, y
     torch.cuda.empty_cache()
     return out
@@ -424,8 +428,51 @@ def mx_run(torch, W, dev, w, x, up, down, what, M, N, K, steps, warmup):
            "quantize_ms": t_q}
     out["fwd_pct_fp4_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_FP4_TFLOPS
     out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
+    out["fwd_small_m"] = small_m_modes(
+        torch, dev, x, N, K, pay, steps, warmup,
+        lambda m: W.fwd_mx4_workspace_bytes(m, p0),
+        lambda xx, yy, wss: W.linear_fwd_mx4(xx, p0, out=yy, workspace=wss))
     del pays, p0, ws, y
     torch.cuda.empty_cache()
+    return out
+
+
+def graph_us(torch, fn, steps, warmup):
+    """GPU time per call of fn(), in microseconds, from one replay of a HIP
+    graph of `steps` back-to-back calls (small calls finish faster than the
+    host enqueues them, so eager timing would measure the host)."""
+    for _ in range(warmup):
+        fn()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(steps):
+                fn()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps * 1e3
+
+
+def small_m_modes(torch, dev, x, N, K, pay, steps, warmup, ws_bytes, fwd, ms=(1, 16, 128)):
+    """Forward of the int8 or MXFP4 payload at small M (first M rows of the
+    layer's activations), graph-replayed; GB/s of payload + x + y."""
+    out = {}
+    for m in ms:
+        xm = x[:m].contiguous()
+        y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(ws_bytes(m), dtype=torch.uint8, device=dev)
+        t = graph_us(torch, lambda: fwd(xm, y, ws), steps, warmup)
+        by = pay + m * K * 2 + m * N * 2
+        out[str(m)] = {"us": t, "gbps": by / (t * 1e-6) / 1e9,
+                       "pct_hbm_peak": 100.0 * by / (t * 1e-6) / 1e9 / PEAK_HBM_GBPS}
     return out
 
 
