@@ -182,6 +182,21 @@ def test_fwd_small_m_tiles():
             _fwd_checks(xbits[:m], codes, scales, upb, dnb, 32, tag=f"m{m} n200 k{k}")
 
 
+def test_fwd_mid_m_plans():
+    # mid-size M with long K: the planner's picks here include 224- and
+    # 256-row tiles with split-K and 224-row tiles without; M and N ragged
+    rng = np.random.default_rng(12)
+    from synth import gen_activations
+    for (m, n, k, g, rank) in [(1500, 1540, 4096, 32, 32), (2000, 1800, 6144, 64, 64),
+                               (2000, 4100, 1024, 32, 0)]:
+        codes, scales, upb, dnb = gen_payload(rng, n, k, g, max(rank, 1))
+        if rank == 0:
+            upb = dnb = None
+        xbits = gen_activations(rng, m, k, 0.01)
+        rows = np.sort(rng.choice(m, 24, replace=False))
+        _fwd_checks(xbits, codes, scales, upb, dnb, g, rows=rows, tag=f"m{m} n{n} k{k} g{g} r{rank}")
+
+
 def test_fwd_decode_shapes():
     # the M <= 16 path: K slices of 512 and 1024 values, whole and with a
     # one-block last slice; N ragged against its 256-row workgroups and its

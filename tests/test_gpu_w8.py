@@ -213,6 +213,19 @@ def test_w8_fwd_tiles_and_splits():
         _fwd_checks(xbits, q, scales, upb, dnb, tag=f"m{m} n{n} k{k} r{rank}")
 
 
+
+def test_w8_fwd_mid_m_plans():
+    # mid-size M with long K (224- and 256-row tiles, with and without split-K)
+    rng = np.random.default_rng(27)
+    for (m, n, k, rank) in [(1500, 1540, 4096, 16), (2000, 1800, 6144, 32), (2000, 4100, 1024, 0)]:
+        q, scales, upb, dnb = gen_payload_w8(rng, n, k, max(rank, 1))
+        if rank == 0:
+            upb = dnb = None
+        xbits = gen_activations(rng, m, k, 0.01)
+        rows = np.sort(rng.choice(m, 24, replace=False))
+        _fwd_checks(xbits, q, scales, upb, dnb, rows=rows, tag=f"m{m} n{n} k{k} r{rank}")
+
+
 def test_w8_end_to_end_quantized_layer():
     # device quantizer -> device forward and reconstruct of its own payload
     import w4_gemm_amd as W
