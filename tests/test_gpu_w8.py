@@ -189,8 +189,24 @@ def _fwd_checks(xbits, q, scales, upb, dnb, rows=None, tag=""):
     return y32h
 
 
+def test_w8_fwd_decode_shapes():
+    # M <= 16: the decode kernel on the int8 payload; N ragged against its
+    # 256-row workgroups and 64-row waves, K slices with a short last slice,
+    # every rank
+    rng = np.random.default_rng(28)
+    for (n, k, rank) in [(1, 256, 16), (200, 3328, 32), (520, 1024, 64), (256, 2304, 0),
+                         (300, 4096, 16)]:
+        q, scales, upb, dnb = gen_payload_w8(rng, n, k, max(rank, 1))
+        if rank == 0:
+            upb = dnb = None
+        xbits = gen_activations(rng, 16, k, 0.01)
+        for m in (1, 2, 5, 16):
+            _fwd_checks(xbits[:m], q, scales, upb, dnb, tag=f"decode m{m} n{n} k{k} r{rank}")
+
+
 def test_w8_fwd_small_m():
-    # M <= 64: the streaming contraction with one, two and four 16-row tiles
+    # M <= 64: the decode kernel (M <= 16), then the streaming contraction
+    # with two and four 16-row tiles
     rng = np.random.default_rng(25)
     for (n, k, rank) in [(200, 1280, 16), (64, 2048, 32), (300, 768, 0), (33, 256, 64)]:
         q, scales, upb, dnb = gen_payload_w8(rng, n, k, max(rank, 1))

@@ -249,9 +249,16 @@ sq_status_t sq_reconstruct_bf16_w8(const sq_w8_t* p, uint16_t* w_hat, void* stre
                                          static_cast<hipStream_t>(stream)));
 }
 
+// group 0 selects the int8 payload in the forward kernels
+static sq::FwdPlan make_fwd_plan_w8(int64_t m, const sq_w8_t* p) {
+  if (sq::decode_eligible(m, p->n, p->k, p->rank, true))
+    return sq::plan_decode(m, p->n, p->k, 0, p->rank);
+  return sq::plan_fwd(m, p->n, p->k, 0, p->rank);
+}
+
 size_t sq_linear_fwd_w8_workspace_bytes(int64_t m, const sq_w8_t* p) {
   if (!p || m <= 0 || p->k < 256 || p->k % 256 || p->n < 1) return 0;
-  return sq::plan_fwd(m, p->n, p->k, 0, p->rank).total;
+  return make_fwd_plan_w8(m, p).total;
 }
 
 sq_status_t sq_linear_fwd_w8(const uint16_t* x, int64_t m, const sq_w8_t* p, void* y,
@@ -264,11 +271,14 @@ sq_status_t sq_linear_fwd_w8(const uint16_t* x, int64_t m, const sq_w8_t* p, voi
   if (m == 0) return SQ_OK;
   if (!x || !y || !workspace) return SQ_E_NULL;
   if (!aligned16(x) || !aligned16(y) || !aligned16(workspace)) return SQ_E_ALIGN;
-  // group 0 selects the int8 payload in the forward kernels
-  const sq::FwdPlan plan = sq::plan_fwd(m, p->n, p->k, 0, p->rank);
+  const sq::FwdPlan plan = make_fwd_plan_w8(m, p);
   if (workspace_bytes < plan.total) return SQ_E_WORKSPACE;
   if ((st = check_device()) != SQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.dec)
+    return from_hip(sq::launch_decode_contract(
+        plan, x, p->lora_down, reinterpret_cast<const uint8_t*>(p->codes), p->scales, p->lora_up,
+        y, y_dtype == SQ_BF16, workspace, s));
   if ((st = from_hip(sq::launch_fwd_rotate(plan, x, p->lora_down, workspace, s))) != SQ_OK)
     return st;
   return from_hip(sq::launch_fwd_contract(plan, reinterpret_cast<const uint8_t*>(p->codes),

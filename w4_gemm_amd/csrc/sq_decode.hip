@@ -242,38 +242,51 @@ __global__ void __launch_bounds__(256) k_fwd_decode(
 
   // ---- codes and scales: lane (fr, g) of wave w reads weight row
   // n0 + 16t + fr, bytes 32g .. 32g+31 of each block's 128-byte line (K
-  // values 64g .. 64g+63 of the block), and the scales of those K values
+  // values 64g .. 64g+63 of the block), and the scales of those K values.
+  // The int8 payload (GSHIFT 0): bytes 64g .. 64g+63 of the block's 256,
+  // one scale per weight row, applied with the row exponent at the end.
+  constexpr int CW = GSHIFT ? 2 : 4;                  // 16-byte code pieces per block and tile
+  constexpr uint32_t BSTR = GSHIFT ? 128u : 256u;     // code bytes of a block's row
   const int64_t n0 = (int64_t)blockIdx.y * 256 + 64 * wave;
-  const int64_t half_k = k >> 1, ngroups = k >> GSHIFT;
+  const int64_t rowb = GSHIFT ? (k >> 1) : k, ngroups = GSHIFT ? (k >> GSHIFT) : 1;
   const int64_t w_rows = std::max<int64_t>(0, std::min<int64_t>(64, n - n0));
   const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(codes + std::min(n0, n) * half_k), (short)0, (int)(w_rows * half_k), 0x00020000);
+      (void*)(codes + std::min(n0, n) * rowb), (short)0, (int)(w_rows * rowb), 0x00020000);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(scales + std::min(n0, n) * ngroups), (short)0, (int)(w_rows * ngroups * 2), 0x00020000);
   uint32_t c_off[4], s_off[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    c_off[t] = (uint32_t)((16 * t + fr) * half_k + (k0 >> 1)) + 32u * g;
+    if constexpr (GSHIFT == 0)
+      c_off[t] = (uint32_t)((16 * t + fr) * rowb + k0) + 64u * g;
+    else
+      c_off[t] = (uint32_t)((16 * t + fr) * rowb + (k0 >> 1)) + 32u * g;
     if constexpr (GSHIFT == 5)
       s_off[t] = (uint32_t)(((16 * t + fr) * ngroups + (k0 >> 5)) * 2) + 4u * g;
-    else
+    else if constexpr (GSHIFT == 6)
       s_off[t] = (uint32_t)(((16 * t + fr) * ngroups + (k0 >> 6)) * 2) + 2u * g;
+    else
+      s_off[t] = 0;
   }
-  // block b: 2 x 16 bytes of codes and the lane's scales (two fp16 of group
+  // block b: CW x 16 bytes of codes and the lane's scales (two fp16 of group
   // size 32 in one word, one of group size 64) per tile; b >= nb reads zeros
-  auto load_blk = [&](u32x4 (&cw)[4][2], uint32_t (&sc)[4], int b) {
+  auto load_blk = [&](u32x4 (&cw)[4][CW], uint32_t (&sc)[4], int b) {
     const uint32_t off = b < nb ? 0u : 0x80000000u;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      cw[t][0] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off + c_off[t] + 128u * b, 0, 0);
-      cw[t][1] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off + c_off[t] + 128u * b + 16u, 0, 0);
+#pragma unroll
+      for (int q = 0; q < CW; ++q)
+        cw[t][q] = __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off + c_off[t] + BSTR * b + 16u * q,
+                                                         0, 0);
       if constexpr (GSHIFT == 5)
         sc[t] = __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, off + s_off[t] + 16u * b, 0, 0);
-      else
+      else if constexpr (GSHIFT == 6)
         sc[t] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, off + s_off[t] + 8u * b, 0, 0);
+      else
+        sc[t] = 0;
     }
   };
-  u32x4 cw[DEC_DEPTH][4][2];
+  u32x4 cw[DEC_DEPTH][4][CW];
   uint32_t sc[DEC_DEPTH][4];
 #pragma unroll
   for (int d = 0; d < DEC_DEPTH; ++d) {
@@ -335,20 +348,37 @@ __global__ void __launch_bounds__(256) k_fwd_decode(
           af[e] = *reinterpret_cast<const half8*>(a_base + 256 * b + 32 * c + 8 * e);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint32_t sbits =
-              GSHIFT == 5 ? (c ? sc[d][t] >> 16 : sc[d][t] & 0xFFFFu) : sc[d][t] & 0xFFFFu;
-          const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sbits);
+          if constexpr (GSHIFT == 0) {
+            // K values 64g + 32c + 8e .. +7: bytes 8e' .. 8e'+7 of piece 2c + e/2
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[e], dequant8_f16(cw[d][t][c][e], sv),
-                                                            acc[t], 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+              const u32x4& pc = cw[d][t][2 * c + (e >> 1)];
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  af[e], dequant8_i8(pc[2 * (e & 1)], pc[2 * (e & 1) + 1]), acc[t], 0, 0, 0);
+            }
+          } else {
+            const uint32_t sbits =
+                GSHIFT == 5 ? (c ? sc[d][t] >> 16 : sc[d][t] & 0xFFFFu) : sc[d][t] & 0xFFFFu;
+            const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)sbits);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[e], dequant8_f16(cw[d][t][c][e], sv),
+                                                              acc[t], 0, 0, 0);
+          }
         }
       }
     }
     if (b + DEC_DEPTH < DEC_NB_MAX) load_blk(cw[d], sc[d], b + DEC_DEPTH);
   }
 
-  // ---- partial[s][row][col] = acc * 2^(E - 11); acc[t][i]: row 4g + i, col n0 + 16t + fr
+  // ---- partial[s][row][col] = acc * 2^(E - 11) (int8: times the weight
+  // row's scale); acc[t][i]: row 4g + i, col n0 + 16t + fr
+  float cs[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t c = n0 + 16 * t + fr;
+    cs[t] = (GSHIFT == 0 && c < n) ? (float)__builtin_bit_cast(_Float16, scales[c]) : 1.0f;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * g + i;
@@ -357,7 +387,8 @@ __global__ void __launch_bounds__(256) k_fwd_decode(
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int64_t c = n0 + 16 * t + fr;
-      if (c < n) partial[((int64_t)s * m + r) * n + c] = acc[t][i] * rs;
+      if (c < n) partial[((int64_t)s * m + r) * n + c] = GSHIFT == 0 ? (acc[t][i] * cs[t]) * rs
+                                                                      : acc[t][i] * rs;
     }
   }
 }
@@ -423,11 +454,11 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
-bool decode_eligible(int64_t m, int64_t n, int64_t k, int rank) {
+bool decode_eligible(int64_t m, int64_t n, int64_t k, int rank, bool int8) {
   // 32-bit buffer offsets: 16 rows of x, one wave's 64 weight rows, lora_down
   return m >= 1 && m <= DEC_MAX_M && DEC_MAX_M * k * 2 < ((int64_t)1 << 31) &&
-         64 * (k >> 1) < ((int64_t)1 << 31) && k * rank * 2 < ((int64_t)1 << 31) &&
-         (rank == 0 || rank == 32 || rank == 64);
+         64 * (int8 ? k : (k >> 1)) < ((int64_t)1 << 31) && k * rank * 2 < ((int64_t)1 << 31) &&
+         (rank == 0 || (int8 && rank == 16) || rank == 32 || rank == 64);
 }
 
 // K slice: the longest (at most 1024 values) that still gives about 1600
@@ -476,6 +507,9 @@ hipError_t launch_decode_contract(const FwdPlan& p, const uint16_t* x, const uin
   const dim3 grid((unsigned)p.splits, (unsigned)(ntiles + (p.rank > 0 ? 1 : 0)));
   if (p.group == 32)
     hipLaunchKernelGGL(k_fwd_decode<5>, grid, dim3(256), 0, stream, x, down, codes, scales, partial,
+                       t_slice, p.m, p.n, p.k, p.rank, p.dec_kslice, ntiles);
+  else if (p.group == 0)
+    hipLaunchKernelGGL(k_fwd_decode<0>, grid, dim3(256), 0, stream, x, down, codes, scales, partial,
                        t_slice, p.m, p.n, p.k, p.rank, p.dec_kslice, ntiles);
   else
     hipLaunchKernelGGL(k_fwd_decode<6>, grid, dim3(256), 0, stream, x, down, codes, scales, partial,

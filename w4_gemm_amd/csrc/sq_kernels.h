@@ -63,7 +63,7 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank);
 // product runs in launch_decode_contract; in the split-call form the first
 // half stages x and lora_down in the workspace (launch_decode_prep) and the
 // second passes x = down = null to read them there.
-bool decode_eligible(int64_t m, int64_t n, int64_t k, int rank);
+bool decode_eligible(int64_t m, int64_t n, int64_t k, int rank, bool int8 = false);
 FwdPlan plan_decode(int64_t m, int64_t n, int64_t k, int group, int rank);
 hipError_t launch_decode_prep(const FwdPlan& plan, const uint16_t* x, const uint16_t* down,
                               void* workspace, hipStream_t stream);
