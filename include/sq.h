@@ -43,7 +43,8 @@ typedef enum {
   SQ_E_SHAPE = 2,     /* K % 256 != 0, K < 256, N < 1 or M < 0; the input         */
                       /* gradient also needs N % 64 == 0                          */
   SQ_E_GROUP = 3,     /* group is not 32 or 64                                    */
-  SQ_E_RANK = 4,      /* rank is not 0, 32 or 64 (the int8 mode also takes 16)    */
+  SQ_E_RANK = 4,      /* rank is not 0, 32 or 64 (the int8 and MXFP4 modes also  */
+                      /* take 16); see the note on ranks below                    */
   SQ_E_ALIGN = 5,     /* a pointer is not 16-byte aligned                         */
   SQ_E_WORKSPACE = 6, /* workspace smaller than the matching *_workspace_bytes()  */
   SQ_E_DTYPE = 7,     /* output dtype is not SQ_F32 or SQ_BF16                    */
@@ -56,9 +57,28 @@ typedef enum { SQ_F32 = 0, SQ_BF16 = 1 } sq_dtype_t;
 /* Bits OR-ed into *dev_flags by the quantizer (read them after a sync). */
 enum {
   SQ_FLAG_NONFINITE = 1,      /* a weight value, or the residual, is NaN or +-inf      */
-  SQ_FLAG_SCALE_OVERFLOW = 2  /* absmax/7 of some group (int8 mode: absmax/127 of some */
+  SQ_FLAG_SCALE_OVERFLOW = 2, /* absmax/7 of some group (int8 mode: absmax/127 of some */
                               /* row) overflows fp16                                   */
+  SQ_FLAG_FP16_RANGE = 4      /* W4 only: some chosen scale exceeds 8188, so the       */
+                              /* payload is outside the forward's domain (below)       */
 };
+
+/* Ranks.  The page's low-rank branch is rank 32.  The W4 entry points take
+ * rank 0, 32 or 64: their kernels walk the factors in 32-wide steps and the
+ * input gradient reads whole steps, so rank 16 is refused with SQ_E_RANK
+ * rather than read past the factors.  The int8 and MXFP4 modes also take 16
+ * (the page's v3.1 split rank).
+ *
+ * Domain of the W4 forward and input gradient.  Their contraction runs on
+ * fp16 MFMA with the weight operand fp16(q * s), q in [-8, 7]; it is finite
+ * for every payload whose scales all satisfy 8 * |s| <= 65504, that is
+ * |s| <= 8188 (the largest fp16 value below 2^13).  A payload with a larger
+ * scale is outside the domain: the products overflow fp16 and y (or dx) holds
+ * +-inf or NaN where such a group contributes.  sq_quantize_weight never
+ * emits such a payload silently: it sets SQ_FLAG_FP16_RANGE.  Scales in the
+ * fp16 subnormal range are inside the domain (q * s is then exact or rounded
+ * once, like any other product).  The reconstruct works in fp32 and has no
+ * such limit. */
 
 /* The W4 payload of one linear layer with N output and K input features.
  *   codes     uint8  [n][k/2]  byte b of a row = (q[2b] & 0xF) | (q[2b+1] & 0xF) << 4,
@@ -88,7 +108,9 @@ typedef struct {
  * Writes p->codes, p->scales and, when fidx != NULL, fidx[n][k/group] = i
  * (uint8).  Non-finite inputs and fp16 scale overflow set bits in *dev_flags
  * (device int32, required; the library only ORs bits into it, so clear it
- * first); outputs are then unspecified but written in bounds. */
+ * first); outputs are then unspecified but written in bounds.  A chosen scale
+ * above 8188 sets SQ_FLAG_FP16_RANGE: the payload is then exact as a format
+ * (reconstruct handles it) but outside the forward's domain. */
 sq_status_t sq_quantize_weight(const float *w, const sq_w4_t *p, uint8_t *fidx,
                                int32_t *dev_flags, void *stream);
 

@@ -61,14 +61,20 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def gen_weight(rng: np.random.Generator, N: int, K: int, spike: int) -> np.ndarray:
-    """W fp32 [N,K]: N(0,1/K) bulk plus a rank-``spike`` component, sigma 8..2."""
+def gen_weight_parts(rng: np.random.Generator, N: int, K: int, spike: int):
+    """(W fp32 [N,K], U [N,s], sigma [s], V [K,s]): the weight of ``gen_weight``
+    together with its planted rank-``spike`` component U diag(sigma) V^T."""
     g = rng.standard_normal((N, K)) / np.sqrt(K)
     u = np.linalg.qr(rng.standard_normal((N, spike)))[0]
     v = np.linalg.qr(rng.standard_normal((K, spike)))[0]
     sig = np.linspace(8.0, 2.0, spike)
     w = g + (u * sig) @ v.T
-    return w.astype(np.float32)
+    return w.astype(np.float32), u, sig, v
+
+
+def gen_weight(rng: np.random.Generator, N: int, K: int, spike: int) -> np.ndarray:
+    """W fp32 [N,K]: N(0,1/K) bulk plus a rank-``spike`` component, sigma 8..2."""
+    return gen_weight_parts(rng, N, K, spike)[0]
 
 
 def gen_activations(rng: np.random.Generator, M: int, K: int, outlier_frac: float) -> np.ndarray:

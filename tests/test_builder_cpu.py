@@ -174,3 +174,50 @@ def test_build_other_codecs(src, tmp_path, fmt, rank):
             assert f.get_tensor(f"{name}.lora_up").shape == (w.shape[0], rank)
     with pytest.raises(ValueError):
         B.build(path, str(tmp_path / "bad"), rank=16, group=32, fmt="w4")
+
+
+class _Stop(Exception):
+    pass
+
+
+def _partial_build(path, out, victim):
+    """Run a build that stops (in process) once `victim`'s first output is written."""
+    def stop(name):
+        if name == victim:
+            raise _Stop()
+    with pytest.raises(_Stop):
+        build(path, out, after_write=stop)
+
+
+def test_resume_refuses_changed_source(src, tmp_path):
+    path, t = src
+    out = str(tmp_path / "slab")
+    _partial_build(path, out, "blocks.1.mlp.down.weight")
+    # same header, different bytes of one tensor
+    t2 = dict(t)
+    t2["blocks.0.attn.q.weight"] = t["blocks.0.attn.q.weight"] * 2
+    from safetensors.torch import save_file
+    save_file(t2, path)
+    assert B.make_plan(path, 32, 32, "exact", ".*").digest == \
+        B.make_plan(path, 32, 32, "exact", ".*").digest
+    with pytest.raises(RuntimeError):
+        build(path, out)
+
+
+def test_resume_rebuilds_a_corrupted_region(src, tmp_path):
+    path, _ = src
+    ref = build(path, str(tmp_path / "ref"))
+    out = str(tmp_path / "slab")
+    _partial_build(path, out, "blocks.1.mlp.down.weight")
+    state = json.load(open(os.path.join(out, B.STATE)))
+    plan = B.make_plan(path, 32, 32, "exact", ".*")
+    victim = next(u for u in plan.units if u.src in state["done"] and u.kind == "w4")
+    with open(os.path.join(out, B.PARTIAL), "r+b") as f:
+        f.seek(plan.data_start + victim.outs[-1].offset + 3)   # a byte of its lora_down
+        b = f.read(1)
+        f.seek(-1, 1)
+        f.write(bytes([b[0] ^ 0x40]))
+    seen = []
+    final = build(path, out, after_write=seen.append)
+    assert victim.src in seen                                   # rebuilt, not trusted
+    assert open(final, "rb").read() == open(ref, "rb").read()

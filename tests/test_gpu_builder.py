@@ -1,9 +1,12 @@
 """The streaming builder with its GPU steps: every quantized tensor of the slab
-equals sq_quantize_weight on the stored factors, bit for bit, and a build
+equals sq_quantize_weight on the stored factors, bit for bit, and matches the
+CPU oracle's quantization of those factors under tie certification; a build
 interrupted from the host resumes to the same bytes."""
 import numpy as np
 import pytest
 import torch
+
+import oracle as O
 
 pytestmark = pytest.mark.gpu
 
@@ -44,6 +47,20 @@ def test_builder_matches_entry_point_and_resumes(tmp_path):
             assert torch.equal(p.codes.cpu(), f.get_tensor(f"{name}.codes"))
             assert torch.equal(p.scales.cpu().view(torch.int16), f.get_tensor(f"{name}.scales").view(torch.int16))
             assert torch.equal(fidx.cpu(), f.get_tensor(f"{name}.fidx"))
+            # and the oracle's quantization of the slab's own factors, tie-certified,
+            # on sampled rows (the whole of the smaller weight)
+            rows = np.arange(w.shape[0]) if w.shape[0] <= 256 else np.sort(
+                np.random.default_rng(1).choice(w.shape[0], 256, replace=False))
+            ups = O.bf16_decode(f.get_tensor(f"{name}.lora_up").view(torch.int16).numpy().view(np.uint16))
+            dns = O.bf16_decode(f.get_tensor(f"{name}.lora_down").view(torch.int16).numpy().view(np.uint16))
+            r = O.residual(t[name].float().numpy()[rows], ups[rows], dns)
+            res = O.quantize_residual(r, 32)
+            rep = O.check_device_quant(
+                r, res, 32, O.unpack(f.get_tensor(f"{name}.codes").numpy()[rows]),
+                f.get_tensor(f"{name}.scales").numpy()[rows].astype(np.float64),
+                f.get_tensor(f"{name}.fidx").numpy()[rows])
+            print(f"{name}: slab vs oracle {rep}")
+            assert rep["ok"], rep
             # the slab reconstructs the weight to the codec's accuracy
             what = W.reconstruct_bf16(p).float()
             e = float((what - w).norm() / w.norm())

@@ -129,6 +129,25 @@ def test_reconstruct_tiny(tiny):
     assert O.cosine(got, exact) > 0.99999
 
 
+@pytest.mark.parametrize("n,k,g,rank", [(100, 768, 64, 32), (16, 256, 64, 0), (33, 1024, 64, 64),
+                                        (50, 512, 32, 0)])
+def test_reconstruct_groups_ranks_ragged(n, k, g, rank):
+    # every element, both group sizes, ranks 0/32/64, N ragged against the 16-row strips
+    import w4_gemm_amd as W
+    rng = np.random.default_rng(n + k + g)
+    codes, scales, upb, dnb = gen_payload(rng, n, k, g, max(rank, 1))
+    if rank == 0:
+        upb = dnb = None
+    p = to_dev_payload(codes, scales, upb, dnb, g)
+    got = bf16_tensor_to_f64(W.reconstruct_bf16(p))
+    torch.cuda.synchronize()
+    q, s, up, dn = payload_fp64(codes, scales, upb, dnb)
+    ref = O.bf16_round(O.reconstruct(q, s, up, dn, g))
+    e = O.rel_fro(got, ref)
+    print(f"reconstruct n{n} k{k} g{g} r{rank}: relF {e:.3e}")
+    assert e <= WHAT_TOL and np.all(np.abs(got - ref) <= ulp_bf16(ref))
+
+
 def _fwd_checks(xbits, codes, scales, upb, dnb, group, rows=None, tag=""):
     import w4_gemm_amd as W
     p = to_dev_payload(codes, scales, upb, dnb, group)
@@ -401,3 +420,45 @@ def test_quantize_cfg3_sampled_rows():
                                fidx[torch.from_numpy(rows).to(d)].cpu().numpy())
     print("cfg3 quantize", rep)
     assert rep["ok"], rep
+
+
+# ------------------------------------------------------------------ fp16 range of the operands
+def _edge_scale_payload(rng, n=64, k=512, g=32, rank=32):
+    """Rows in four bands of scales: 8188 (the largest with 8 s <= 65504, with
+    code -8 present), 2^-20 (fp16 subnormal), 2^-14 (smallest normal), 1e-3."""
+    q = rng.integers(-8, 8, (n, k))
+    q[:16, ::g] = -8
+    bands = [8188.0, 2.0 ** -20, 2.0 ** -14, float(np.float16(1e-3))]
+    s = np.repeat(np.array(bands), n // 4)[:, None] * np.ones((1, k // g))
+    codes = O.pack(q)
+    scales = s.astype(np.float16)
+    up = bf16_bits_of(O.bf16_round(rng.standard_normal((n, rank)) * 0.1))
+    dn = bf16_bits_of(O.bf16_round(rng.standard_normal((k, rank)) * 0.1))
+    return codes, scales, up, dn
+
+
+def test_fwd_and_dgrad_at_scale_range_edges():
+    rng = np.random.default_rng(31)
+    codes, scales, upb, dnb = _edge_scale_payload(rng)
+    from synth import gen_activations
+    for m in (3, 40, 200):
+        xbits = gen_activations(rng, m, 512, 0.01)
+        _fwd_checks(xbits, codes, scales, upb, dnb, 32, tag=f"scale edges m{m}")
+        _dgrad_checks(_gen_dy(rng, m, 64), codes, scales, upb, dnb, 32, tag=f"scale edges m{m}")
+
+
+def test_quantize_fp16_range_flag():
+    import w4_gemm_amd as W
+    rng = np.random.default_rng(32)
+    n, k, g = 16, 512, 32
+    q = rng.integers(-7, 8, (n, k)); q[:, ::g] = 7
+    d = dev()
+    for s, want in ((8188.0, 0), (9000.0, 4)):
+        w = O.rotate(q * s).astype(np.float32)            # rank 0, grid-planted: f = 1.00 exact
+        p, fidx, flags = W.quantize_weight(torch.from_numpy(w).to(d), None, None, g)
+        torch.cuda.synchronize()
+        assert int(flags[0]) == want, (s, int(flags[0]))
+        assert np.all(p.scales.cpu().numpy().astype(np.float64) == s)
+        # the reconstruct (fp32) is exact for either payload
+        what = bf16_tensor_to_f64(W.reconstruct_bf16(p))
+        assert np.array_equal(what, O.bf16_round(O.rotate(q * s)))

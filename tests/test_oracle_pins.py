@@ -641,6 +641,80 @@ def pin_mx_certification():
     assert not O.check_device_mx(a, c3, e2)["ok"]
 
 
+# ----------------------------------------------------------------- metrics and decoders
+def pin_metrics_closed_forms():
+    # rel_F(a, b) = ||a - b|| / ||b||: normalised by the second argument
+    b = np.array([3.0, 4.0])                          # ||b|| = 5
+    a = np.array([3.0, 5.0])                          # ||a - b|| = 1, ||a|| = sqrt(34)
+    assert O.rel_fro(a, b) == 0.2
+    assert abs(O.rel_fro(b, a) - 1 / np.sqrt(34)) < 1e-15
+    assert O.rel_fro(b, b) == 0.0
+    assert O.rel_fro(2 * b, b) == 1.0 and O.rel_fro(-b, b) == 2.0
+    # the Frobenius norm of a matrix is that of its flattened entries
+    m = np.array([[1.0, 2.0], [2.0, 4.0]])            # ||m||_F = 5
+    assert O.rel_fro(m + np.array([[0.0, 0.0], [0.0, 3.0]]), m) == 0.6
+    # cos = <a, b> / (||a|| ||b||): scale-free, signed
+    assert O.cosine([1.0, 0.0], [0.0, 7.0]) == 0.0
+    assert abs(O.cosine([2.0, 0.0], [1.0, 1.0]) - 1 / np.sqrt(2)) < 1e-15
+    assert abs(O.cosine(3 * b, b) - 1.0) < 1e-15 and abs(O.cosine(-b, 0.5 * b) + 1.0) < 1e-15
+    assert abs(O.cosine(m, m.T) - 1.0) < 1e-15       # symmetric: same flattened vector
+    assert abs(O.cosine([[1.0, 2.0], [3.0, 4.0]], [[1.0, 3.0], [2.0, 4.0]]) - 29 / 30) < 1e-15
+
+
+def _fp16_by_formula(bits):
+    """IEEE binary16 value of each 16-bit pattern: sign, 5-bit biased exponent, 10-bit fraction."""
+    bits = np.asarray(bits, np.int64)
+    sgn = np.where(bits >> 15, -1.0, 1.0)
+    e = (bits >> 10) & 31
+    f = (bits & 1023).astype(np.float64)
+    v = np.where(e == 0, f * 2.0 ** -24, (1 + f / 1024) * np.ldexp(1.0, (e - 15).astype(np.int64)))
+    v = np.where(e == 31, np.where(f == 0, np.inf, np.nan), v)
+    return sgn * v
+
+
+def _bf16_by_formula(bits):
+    """bfloat16 value of each 16-bit pattern: sign, 8-bit biased exponent, 7-bit fraction."""
+    bits = np.asarray(bits, np.int64)
+    sgn = np.where(bits >> 15, -1.0, 1.0)
+    e = (bits >> 7) & 255
+    f = (bits & 127).astype(np.float64)
+    v = np.where(e == 0, f * 2.0 ** -133, (1 + f / 128) * np.ldexp(1.0, (e - 127).astype(np.int64)))
+    v = np.where(e == 255, np.where(f == 0, np.inf, np.nan), v)
+    return sgn * v
+
+
+def pin_fp16_bf16_decode_all_patterns():
+    allbits = np.arange(65536).astype(np.uint16)
+    assert np.array_equal(O.fp16_decode(allbits), _fp16_by_formula(allbits), equal_nan=True)
+    assert np.array_equal(O.bf16_decode(allbits), _bf16_by_formula(allbits), equal_nan=True)
+    # an fp16 array decodes to its own values
+    h = np.array([0.5, -3.25, 65504.0, 2.0 ** -24], np.float16)
+    assert list(O.fp16_decode(h)) == [0.5, -3.25, 65504.0, 2.0 ** -24]
+
+
+def pin_w8_fp16_operand_forward():
+    rng = np.random.default_rng(26)
+    n, k, m = 20, 512, 6
+    q = rng.integers(-128, 128, (n, k)).astype(np.float64)
+    sc = O.fp16_round(rng.uniform(1e-3, 1e-2, n))
+    up = O.bf16_round(rng.standard_normal((n, 16)) * 0.1)
+    dn = O.bf16_round(rng.standard_normal((k, 16)) * 0.1)
+    # activations whose rotation is fp16-exact after the row power of two:
+    # then the diagnostic forward equals the exact one
+    xi = O.rotate(rng.integers(-40, 41, (m, k)).astype(np.float64) / 4)
+    np.testing.assert_allclose(O.forward_w8_fp16_operands(xi, q, sc, up, dn),
+                               O.forward_w8(xi, q, sc, up, dn), rtol=1e-12, atol=1e-12)
+    # in general only the rotated activations round (relative 2^-11 each)
+    x = O.bf16_round(rng.standard_normal((m, k)) * 5)
+    y = O.forward_w8(x, q, sc, up, dn)
+    yd = O.forward_w8_fp16_operands(x, q, sc, up, dn)
+    xh = O.rotate(x)
+    bound = (np.abs(xh) @ np.abs(q).T) * np.abs(sc)[None, :] * 2.0 ** -11
+    assert np.all(np.abs(yd - y) <= bound * (1 + 1e-9))
+    e = O.rel_fro(yd, y)
+    assert 1e-6 < e < 2.0 ** -11
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -745,7 +819,45 @@ def _mutations():
     def act_unrotated(x):
         return O.mx_quantize(np.asarray(x, float))
 
+    def rel_fro_by_a(a, b):
+        a = np.asarray(a, float).ravel(); b = np.asarray(b, float).ravel()
+        return float(np.linalg.norm(a - b) / np.linalg.norm(a))
+
+    def rel_fro_squared(a, b):
+        a = np.asarray(a, float).ravel(); b = np.asarray(b, float).ravel()
+        return float((np.linalg.norm(a - b) / np.linalg.norm(b)) ** 2)
+
+    def cosine_one_norm(a, b):
+        a = np.asarray(a, float).ravel(); b = np.asarray(b, float).ravel()
+        return float(a @ b / np.linalg.norm(b) ** 2)
+
+    def fp16_decode_as_int(h):
+        return np.asarray(h).astype(np.float64)
+
+    def bf16_decode_low_half(bits):
+        b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+        return b.view(np.float32).astype(np.float64)
+
+    orig_fwd8d = O.sq_oracle.forward_w8_fp16_operands
+
+    def fwd8_scale_twice(x, q, scale, up, down):
+        y = orig_fwd8d(x, q, scale, up, down)
+        lr = (np.asarray(x, float) @ down) @ up.T
+        return (y - lr) * np.asarray(scale, float)[None, :] + lr
+
+    def fwd8_bf16_operands(x, q, scale, up, down):
+        x = np.asarray(x, float)
+        xh = O.bf16_round(O.rotate(x))
+        return (xh @ np.asarray(q, float).T) * np.asarray(scale, float)[None, :] + (x @ down) @ up.T
+
     return [
+        ("rel_fro", rel_fro_by_a),
+        ("rel_fro", rel_fro_squared),
+        ("cosine", cosine_one_norm),
+        ("fp16_decode", fp16_decode_as_int),
+        ("bf16_decode", bf16_decode_low_half),
+        ("forward_w8_fp16_operands", fwd8_scale_twice),
+        ("forward_w8_fp16_operands", fwd8_bf16_operands),
         ("e2m1_encode", e2m1_ties_away),
         ("mx_scale_exponent", mx_scale_ceil),
         ("mx_scale_exponent", mx_scale_emax3),

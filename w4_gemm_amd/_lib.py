@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libsq.so")
 
 SQ_OK = 0
 SQ_F32, SQ_BF16 = 0, 1
-SQ_FLAG_NONFINITE, SQ_FLAG_SCALE_OVERFLOW = 1, 2
+SQ_FLAG_NONFINITE, SQ_FLAG_SCALE_OVERFLOW, SQ_FLAG_FP16_RANGE = 1, 2, 4
 STATUS_NAMES = {0: "SQ_OK", 1: "SQ_E_NULL", 2: "SQ_E_SHAPE", 3: "SQ_E_GROUP", 4: "SQ_E_RANK",
                 5: "SQ_E_ALIGN", 6: "SQ_E_WORKSPACE", 7: "SQ_E_DTYPE", 8: "SQ_E_ARCH",
                 9: "SQ_E_HIP"}

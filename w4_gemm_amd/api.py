@@ -11,6 +11,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
+from . import shapes as S
 from ._lib import SqError, SqMx4, SqW4, SqW8, SQ_BF16, SQ_F32
 
 
@@ -38,6 +39,8 @@ class W4Payload:
     def abi(self) -> SqW4:
         _require(self.codes, torch.uint8, "codes")
         _require(self.scales, torch.float16, "scales")
+        S.check_w4_payload(self.codes.shape, self.scales.shape, _shp(self.up), _shp(self.down),
+                           self.group)
         if self.up is not None:
             _require(self.up, torch.bfloat16, "up")
             _require(self.down, torch.bfloat16, "down")
@@ -57,6 +60,16 @@ def _require(t, dtype, name):
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
+
+
+def _shp(t):
+    return None if t is None else tuple(t.shape)
+
+
+def _nbytes(t):
+    """Byte size of a caller's workspace tensor (dense, on the device)."""
+    _require(t, t.dtype, "workspace")
+    return t.numel() * t.element_size()
 
 
 def _stream():
@@ -80,8 +93,7 @@ def quantize_weight(w: torch.Tensor, up: torch.Tensor | None, down: torch.Tensor
                     group: int, want_fidx: bool = True):
     """sq_quantize_weight: fp32 W [N,K] and bf16 factors -> (payload, fidx, flags tensor)."""
     _require(w, torch.float32, "w")
-    n, k = w.shape
-    rank = 0 if up is None else up.shape[1]
+    n, k, rank = S.check_weight(w.shape, _shp(up), _shp(down))
     p = empty_payload(n, k, group, rank, w.device)
     p.up, p.down = up, down
     fidx = torch.empty((n, k // group), dtype=torch.uint8, device=w.device) if want_fidx else None
@@ -99,7 +111,7 @@ def linear_fwd(x: torch.Tensor, p: W4Payload, out_dtype=torch.float32,
                workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
     """sq_linear_fwd: bf16 x [M,K] -> y [M,N] (fp32 or bf16)."""
     _require(x, torch.bfloat16, "x")
-    m = x.shape[0]
+    m = S.check_rows("x", x.shape, p.k)
     if out is None:
         out = torch.empty((m, p.n), dtype=out_dtype, device=x.device)
     _require(out, out.dtype, "out")
@@ -110,23 +122,29 @@ def linear_fwd(x: torch.Tensor, p: W4Payload, out_dtype=torch.float32,
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
     _check(_lib.sq_linear_fwd(x.data_ptr(), m, p.abi(), out.data_ptr(), dt, workspace.data_ptr(),
-                              workspace.numel(), _stream()), "sq_linear_fwd")
+                              _nbytes(workspace), _stream()), "sq_linear_fwd")
     return out
 
 
 def linear_fwd_rotate(x: torch.Tensor, p: W4Payload, workspace: torch.Tensor):
     """sq_linear_fwd_rotate: the activation half of the forward, into `workspace`."""
     _require(x, torch.bfloat16, "x")
+    S.check_rows("x", x.shape, p.k)
     _check(_lib.sq_linear_fwd_rotate(x.data_ptr(), x.shape[0], p.abi(), workspace.data_ptr(),
-                                     workspace.numel(), _stream()), "sq_linear_fwd_rotate")
+                                     _nbytes(workspace), _stream()),
+           "sq_linear_fwd_rotate")
 
 
 def linear_fwd_contract(m: int, p: W4Payload, out: torch.Tensor, workspace: torch.Tensor):
     """sq_linear_fwd_contract: the weight half of the forward, from `workspace` into out."""
     _require(out, out.dtype, "out")
+    S.check_out("out", out.shape, (m, p.n))
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out must be fp32 or bf16")
     dt = SQ_BF16 if out.dtype == torch.bfloat16 else SQ_F32
     _check(_lib.sq_linear_fwd_contract(m, p.abi(), out.data_ptr(), dt, workspace.data_ptr(),
-                                       workspace.numel(), _stream()), "sq_linear_fwd_contract")
+                                       _nbytes(workspace), _stream()),
+           "sq_linear_fwd_contract")
     return out
 
 
@@ -138,7 +156,7 @@ def linear_dgrad(dy: torch.Tensor, p: W4Payload, out_dtype=torch.float32,
                  workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
     """sq_linear_dgrad: bf16 dy [M,N] -> dx = dy @ W_hat [M,K] (fp32 or bf16)."""
     _require(dy, torch.bfloat16, "dy")
-    m = dy.shape[0]
+    m = S.check_rows("dy", dy.shape, p.n)
     if out is None:
         out = torch.empty((m, p.k), dtype=out_dtype, device=dy.device)
     _require(out, out.dtype, "out")
@@ -149,7 +167,7 @@ def linear_dgrad(dy: torch.Tensor, p: W4Payload, out_dtype=torch.float32,
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dy.device)
     _check(_lib.sq_linear_dgrad(dy.data_ptr(), m, p.abi(), out.data_ptr(), dt,
-                                workspace.data_ptr(), workspace.numel(), _stream()),
+                                workspace.data_ptr(), _nbytes(workspace), _stream()),
            "sq_linear_dgrad")
     return out
 
@@ -159,6 +177,7 @@ def reconstruct_bf16(p: W4Payload, out: torch.Tensor | None = None):
     if out is None:
         out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device=p.codes.device)
     _require(out, torch.bfloat16, "out")
+    S.check_out("out", out.shape, (p.n, p.k))
     _check(_lib.sq_reconstruct_bf16(p.abi(), out.data_ptr(), _stream()), "sq_reconstruct_bf16")
     return out
 
@@ -187,6 +206,7 @@ class W8Payload:
     def abi(self) -> SqW8:
         _require(self.codes, torch.int8, "codes")
         _require(self.scales, torch.float16, "scales")
+        S.check_w8_payload(self.codes.shape, self.scales.shape, _shp(self.up), _shp(self.down))
         if self.up is not None:
             _require(self.up, torch.bfloat16, "up")
             _require(self.down, torch.bfloat16, "down")
@@ -205,8 +225,7 @@ def quantize_weight_w8(w: torch.Tensor, up: torch.Tensor | None, down: torch.Ten
                        want_fidx: bool = True, workspace: torch.Tensor | None = None):
     """sq_quantize_weight_w8: fp32 W [N,K] and bf16 factors -> (payload, fidx, flags tensor)."""
     _require(w, torch.float32, "w")
-    n, k = w.shape
-    rank = 0 if up is None else up.shape[1]
+    n, k, rank = S.check_weight(w.shape, _shp(up), _shp(down), (16, 32, 64))
     p = empty_payload_w8(n, k, rank, w.device)
     p.up, p.down = up, down
     fidx = torch.empty((n,), dtype=torch.uint8, device=w.device) if want_fidx else None
@@ -215,7 +234,7 @@ def quantize_weight_w8(w: torch.Tensor, up: torch.Tensor | None, down: torch.Ten
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=w.device)
     _check(_lib.sq_quantize_weight_w8(w.data_ptr(), p.abi(), _ptr(fidx), flags.data_ptr(),
-                                      workspace.data_ptr(), workspace.numel(), _stream()),
+                                      workspace.data_ptr(), _nbytes(workspace), _stream()),
            "sq_quantize_weight_w8")
     return p, fidx, flags
 
@@ -225,6 +244,7 @@ def reconstruct_bf16_w8(p: W8Payload, out: torch.Tensor | None = None):
     if out is None:
         out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device=p.codes.device)
     _require(out, torch.bfloat16, "out")
+    S.check_out("out", out.shape, (p.n, p.k))
     _check(_lib.sq_reconstruct_bf16_w8(p.abi(), out.data_ptr(), _stream()),
            "sq_reconstruct_bf16_w8")
     return out
@@ -238,7 +258,7 @@ def linear_fwd_w8(x: torch.Tensor, p: W8Payload, out_dtype=torch.float32,
                   workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
     """sq_linear_fwd_w8: bf16 x [M,K] -> y [M,N] (fp32 or bf16) for an int8-mode payload."""
     _require(x, torch.bfloat16, "x")
-    m = x.shape[0]
+    m = S.check_rows("x", x.shape, p.k)
     if out is None:
         out = torch.empty((m, p.n), dtype=out_dtype, device=x.device)
     _require(out, out.dtype, "out")
@@ -249,7 +269,7 @@ def linear_fwd_w8(x: torch.Tensor, p: W8Payload, out_dtype=torch.float32,
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
     _check(_lib.sq_linear_fwd_w8(x.data_ptr(), m, p.abi(), out.data_ptr(), dt,
-                                 workspace.data_ptr(), workspace.numel(), _stream()),
+                                 workspace.data_ptr(), _nbytes(workspace), _stream()),
            "sq_linear_fwd_w8")
     return out
 
@@ -278,6 +298,7 @@ class MX4Payload:
     def abi(self) -> SqMx4:
         _require(self.codes, torch.uint8, "codes")
         _require(self.exps, torch.uint8, "exps")
+        S.check_mx4_payload(self.codes.shape, self.exps.shape, _shp(self.up), _shp(self.down))
         if self.up is not None:
             _require(self.up, torch.bfloat16, "up")
             _require(self.down, torch.bfloat16, "down")
@@ -295,8 +316,7 @@ def empty_payload_mx4(n: int, k: int, rank: int, device="cuda") -> MX4Payload:
 def quantize_weight_mx4(w: torch.Tensor, up: torch.Tensor | None, down: torch.Tensor | None):
     """sq_quantize_weight_mx4: fp32 W [N,K] and bf16 factors -> (payload, flags tensor)."""
     _require(w, torch.float32, "w")
-    n, k = w.shape
-    rank = 0 if up is None else up.shape[1]
+    n, k, rank = S.check_weight(w.shape, _shp(up), _shp(down), (16, 32, 64))
     p = empty_payload_mx4(n, k, rank, w.device)
     p.up, p.down = up, down
     flags = torch.zeros(4, dtype=torch.int32, device=w.device)
@@ -308,6 +328,8 @@ def quantize_weight_mx4(w: torch.Tensor, up: torch.Tensor | None, down: torch.Te
 def quantize_act_mx4(x: torch.Tensor):
     """sq_quantize_act_mx4: bf16 x [M,K] -> (uint8 codes [M,K/2], uint8 exps [M,K/32]) of x @ H."""
     _require(x, torch.bfloat16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
     m, k = x.shape
     xq = torch.empty((m, k // 2), dtype=torch.uint8, device=x.device)
     xs = torch.empty((m, k // 32), dtype=torch.uint8, device=x.device)
@@ -321,6 +343,7 @@ def reconstruct_bf16_mx4(p: MX4Payload, out: torch.Tensor | None = None):
     if out is None:
         out = torch.empty((p.n, p.k), dtype=torch.bfloat16, device=p.codes.device)
     _require(out, torch.bfloat16, "out")
+    S.check_out("out", out.shape, (p.n, p.k))
     _check(_lib.sq_reconstruct_bf16_mx4(p.abi(), out.data_ptr(), _stream()),
            "sq_reconstruct_bf16_mx4")
     return out
@@ -334,7 +357,7 @@ def linear_fwd_mx4(x: torch.Tensor, p: MX4Payload, out_dtype=torch.float32,
                    workspace: torch.Tensor | None = None, out: torch.Tensor | None = None):
     """sq_linear_fwd_mx4: bf16 x [M,K] -> y [M,N] (fp32 or bf16) for an MXFP4 payload."""
     _require(x, torch.bfloat16, "x")
-    m = x.shape[0]
+    m = S.check_rows("x", x.shape, p.k)
     if out is None:
         out = torch.empty((m, p.n), dtype=out_dtype, device=x.device)
     _require(out, out.dtype, "out")
@@ -345,6 +368,6 @@ def linear_fwd_mx4(x: torch.Tensor, p: MX4Payload, out_dtype=torch.float32,
     if workspace is None:
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
     _check(_lib.sq_linear_fwd_mx4(x.data_ptr(), m, p.abi(), out.data_ptr(), dt,
-                                  workspace.data_ptr(), workspace.numel(), _stream()),
+                                  workspace.data_ptr(), _nbytes(workspace), _stream()),
            "sq_linear_fwd_mx4")
     return out

@@ -35,8 +35,12 @@ Restart protocol (`<out_dir>/slab.safetensors.partial` during the build,
 A kill at any point loses at most the tensor in progress; its region is
 rewritten on the next run.  Every tensor's bytes are a deterministic function
 of the source bytes and the options, so a resumed build is byte-identical to
-an uninterrupted one.  Peak host memory is about one source tensor and its
-outputs.
+an uninterrupted one.  The state file also records the source's size and the
+sha256 of every source tensor's bytes: a resume against a source whose
+contents changed (even with an identical header) is refused, and every
+recorded tensor's output region is re-hashed against its recorded sha256
+before it is trusted (a mismatch is rebuilt).  Peak host memory is about one
+source tensor and its outputs.
 
 Usage: python -m w4_gemm_amd.builder --src model.safetensors --out-dir slab \
            [--format w4|int8|mxfp4] [--rank 32] [--group 32] [--svd auto|exact|randomized]
@@ -66,6 +70,8 @@ ITEMSIZE = {"F32": 4, "F16": 2, "BF16": 2, "U8": 1, "I8": 1, "F64": 8, "I32": 4,
             "U16": 2, "I16": 2, "BOOL": 1}
 FLOAT_IN = ("F32", "F16", "BF16")
 EXACT_SVD_MAX = 1 << 22   # weights with at most this many elements get the host fp64 SVD
+RSVD_OVERSAMPLE = 96      # randomized split: extra sample columns beyond the rank
+RSVD_ITERS = 16           # randomized split: power iterations
 
 
 # ---------------------------------------------------------------- safetensors header
@@ -179,9 +185,11 @@ def gpu_lowrank(w: np.ndarray, rank: int, name: str, svd: str):
     """bf16 bit patterns (up [N,r], down [K,r]) of the rank-r split U sqrt(S), V sqrt(S).
 
     exact: host fp64 LAPACK SVD, one rounding to bf16.  randomized: a seeded
-    randomized SVD on the GPU in fp32 (q = r + 8 samples, two power
-    iterations, seed from the tensor name), for weights too large for the
-    host SVD; the residual absorbs any difference from the exact factors.
+    randomized SVD on the GPU in fp64 (r + RSVD_OVERSAMPLE sample columns,
+    RSVD_ITERS power iterations, seed from the tensor name), for weights too
+    large for the host SVD.  Its rank-r residual energy stays within 1e-4 of
+    the Eckart-Young optimum on the layer distributions (pinned on the CPU);
+    the residual absorbs any difference from the exact factors.
     """
     import torch
     if svd == "auto":
@@ -191,13 +199,18 @@ def gpu_lowrank(w: np.ndarray, rank: int, name: str, svd: str):
         up, dn = svd_init(w, rank)
         return (up.view(torch.int16).numpy().view(np.uint16), dn.view(torch.int16).numpy().view(np.uint16))
     g = torch.Generator(device="cuda").manual_seed(zlib.crc32(name.encode()))
-    wd = torch.from_numpy(w).cuda()
-    u, s, v = _svd_lowrank(torch, wd, rank + 8, g)
+    wd = torch.from_numpy(w).cuda().double()
+    u, s, v = randomized_split(torch, wd, rank, g)
     r = s[:rank].sqrt()
-    up = (u[:, :rank] * r).to(torch.bfloat16).contiguous()
-    dn = (v[:, :rank] * r).to(torch.bfloat16).contiguous()
-    return (up.view(torch.int16).cpu().numpy().view(np.uint16),
-            dn.view(torch.int16).cpu().numpy().view(np.uint16))
+    from .svd_init import _bf16_from_f64      # one rounding from fp64, as the exact split
+    up = _bf16_from_f64((u[:, :rank] * r).cpu().numpy())
+    dn = _bf16_from_f64((v[:, :rank] * r).cpu().numpy())
+    return up.view(torch.int16).numpy().view(np.uint16), dn.view(torch.int16).numpy().view(np.uint16)
+
+
+def randomized_split(torch, a, rank: int, gen):
+    """Top singular triplets of `a` by the randomized range finder below."""
+    return _svd_lowrank(torch, a, min(rank + RSVD_OVERSAMPLE, min(a.shape)), gen, RSVD_ITERS)
 
 
 def _svd_lowrank(torch, a, q, gen, niter=2):
@@ -267,6 +280,24 @@ GPU_QUANTIZE = {"w4": gpu_quantize, "int8": gpu_quantize_w8, "mxfp4": gpu_quanti
 
 
 # ---------------------------------------------------------------- the build
+def source_digest(src: str) -> str:
+    """sha256 over the source's size and the sha256 of each tensor's bytes, in name order."""
+    hdr, _, start = read_header(src)
+    h = hashlib.sha256(str(os.path.getsize(src)).encode())
+    with open(src, "rb") as f, mmap.mmap(f.fileno(), 0, access=mmap.ACCESS_READ) as m:
+        for name in sorted(hdr):
+            a, b = hdr[name]["data_offsets"]
+            h.update(name.encode() + b"\0" + hashlib.sha256(m[start + a:start + b]).digest())
+    return h.hexdigest()
+
+
+def _region_sha(fd: int, plan: Plan, unit: Unit) -> str:
+    h = hashlib.sha256()
+    for o in unit.outs:
+        h.update(os.pread(fd, o.nbytes, plan.data_start + o.offset))
+    return h.hexdigest()
+
+
 def _write_state(out_dir: str, state: dict):
     tmp = os.path.join(out_dir, STATE + ".tmp")
     with open(tmp, "w") as f:
@@ -305,11 +336,12 @@ def build(src: str, out_dir: str, rank: int = 32, group: int = 32, svd: str = "a
     plan = make_plan(src, rank, group, svd, include, fmt)
     final, partial = os.path.join(out_dir, SLAB), os.path.join(out_dir, PARTIAL)
     spath = os.path.join(out_dir, STATE)
+    sdig = source_digest(src)
     state = None
     if os.path.exists(spath):
         with open(spath) as f:
             state = json.load(f)
-        if state.get("plan") != plan.digest:
+        if state.get("plan") != plan.digest or state.get("source") != sdig:
             raise RuntimeError(f"{out_dir} holds a build of different inputs or options; "
                                "remove it or choose another directory")
         if state.get("complete") and os.path.exists(final):
@@ -320,8 +352,20 @@ def build(src: str, out_dir: str, rank: int = 32, group: int = 32, svd: str = "a
             f.truncate(plan.data_start + plan.total)
             f.flush()
             os.fsync(f.fileno())
-        state = {"plan": plan.digest, "done": {}, "complete": False}
+        state = {"plan": plan.digest, "source": sdig, "done": {}, "complete": False}
         _write_state(out_dir, state)
+    else:
+        # trust a recorded tensor only if its bytes on disk still hash to the record
+        fd = os.open(partial, os.O_RDONLY)
+        try:
+            stale = [u.src for u in plan.units
+                     if u.src in state["done"] and _region_sha(fd, plan, u) != state["done"][u.src]]
+        finally:
+            os.close(fd)
+        for name in stale:
+            del state["done"][name]
+        if stale:
+            _write_state(out_dir, state)
     _, _, src_start = read_header(src)
     t0 = time.time()
     with open(src, "rb") as sf, mmap.mmap(sf.fileno(), 0, access=mmap.ACCESS_READ) as sm:

@@ -115,6 +115,9 @@ __global__ void __launch_bounds__(256) k_quantize(const float* __restrict__ w,
     sweep_group<64>(v, 0, s0, i0, flags);
   }
 
+  // the forward's fp16(q s) stays finite only while 8 s <= 65504
+  if (s0 > 8188.0f || s1 > 8188.0f) flags |= 4;
+
   // codes of the chosen scales, packed two per byte (even column low)
   u32x4 out[2];
   const float inv0 = s0 > 0.0f ? 1.0f / s0 : 0.0f;

@@ -162,8 +162,12 @@ __device__ __forceinline__ void load_strip(StripIn<GROUP>& in, const uint8_t* cb
   in.w[1] = src[1];
   if (GROUP == 32) {
     in.s2 = *reinterpret_cast<const uint32_t*>(sbase + 2 * g);
+  } else if (GROUP == 64) {
+    // one scale covers the lane's whole 64-value chunk: both halves
+    const uint32_t sv = sbase[g];
+    in.s2 = sv | (sv << 16);
   } else {
-    in.s2 = sbase[g];
+    in.s2 = sbase[g];   // MX: one 16-bit word holds the chunk's two exponents
   }
 }
 
