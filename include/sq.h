@@ -147,6 +147,23 @@ sq_status_t sq_linear_fwd_rotate(const uint16_t *x, int64_t m, const sq_w4_t *p,
 sq_status_t sq_linear_fwd_contract(int64_t m, const sq_w4_t *p, void *y, sq_dtype_t y_dtype,
                                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* The forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  It computes exactly what sq_linear_fwd computes
+ * (same kernels, bit-identical y) with its scratch in a library-owned static
+ * device array of SQ_FWD_STATIC_SCRATCH_BYTES (64 MiB), one per device, held
+ * by each device the library runs on until the process ends.  It allocates
+ * nothing itself; its first call on a device looks up that device's copy of
+ * the array.  A call whose sq_linear_fwd_workspace_bytes(m, p) exceeds the
+ * array returns SQ_E_WORKSPACE and launches nothing (every m <= 16 forward
+ * fits, and so does 4480 x 16384 x 6144).  All calls on one device share the
+ * array: calls ordered on one stream are fine, calls that overlap in time on
+ * one device (different streams, no ordering) race and give undefined y.
+ * Nothing in the array needs to be zero: each call writes what it reads. */
+#define SQ_FWD_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+sq_status_t sq_linear_fwd_static(const uint16_t *x, int64_t m, const sq_w4_t *p, void *y,
+                                 sq_dtype_t y_dtype, void *stream);
+
 /* Backward side: rebuild the dense bf16 weight from the same payload
  *   w_hat[n][k] = bf16_round_nearest_even( lora_up @ lora_down^T + dequant(R) @ H )
  * with every intermediate in fp32 and one rounding at the end. */

@@ -199,3 +199,21 @@ def test_mx_other_arguments():
         pr = _payload_mx(rank=rank, up=None if rank == 0 else 0x3000,
                          down=None if rank == 0 else 0x4000)
         assert _lib.sq_linear_fwd_mx4_workspace_bytes(4, pr) > 0
+
+
+def test_static_forward_arguments():
+    # validation and the scratch limit come before any HIP call
+    p = _payload()
+    assert _lib.sq_linear_fwd_static(0x8000, 0, p, 0x9000, 0, None) == 0      # m == 0: no-op
+    assert _lib.sq_linear_fwd_static(0x8000, -1, p, 0x9000, 0, None) == 2
+    assert _lib.sq_linear_fwd_static(0x8000, 4, p, 0x9000, 5, None) == 7
+    assert _lib.sq_linear_fwd_static(None, 4, p, 0x9000, 0, None) == 1
+    assert _lib.sq_linear_fwd_static(0x8000, 4, p, 0x9008, 0, None) == 5
+    assert _lib.sq_linear_fwd_static(0x8000, 4, _payload(rank=16), 0x9000, 0, None) == 4
+    big = _payload(n=6144, k=16384)                   # 4480 rows need ~146 MB of scratch
+    assert _lib.sq_linear_fwd_workspace_bytes(4480, big) > _lib.SQ_FWD_STATIC_SCRATCH_BYTES
+    assert _lib.sq_linear_fwd_static(0x8000, 4480, big, 0x9000, 0, None) == 6
+    head = _payload(n=16384, k=6144)
+    assert _lib.sq_linear_fwd_workspace_bytes(4480, head) <= _lib.SQ_FWD_STATIC_SCRATCH_BYTES
+    for m in (1, 16):
+        assert _lib.sq_linear_fwd_workspace_bytes(m, big) <= _lib.SQ_FWD_STATIC_SCRATCH_BYTES

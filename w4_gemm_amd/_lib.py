@@ -25,7 +25,8 @@ EXPORTS = ("sq_quantize_weight", "sq_linear_fwd_workspace_bytes", "sq_linear_fwd
            "sq_abi_version", "sq_quantize_weight_w8_workspace_bytes", "sq_quantize_weight_w8",
            "sq_reconstruct_bf16_w8", "sq_linear_fwd_w8_workspace_bytes", "sq_linear_fwd_w8",
            "sq_quantize_weight_mx4", "sq_quantize_act_mx4", "sq_reconstruct_bf16_mx4",
-           "sq_linear_fwd_mx4_workspace_bytes", "sq_linear_fwd_mx4")
+           "sq_linear_fwd_mx4_workspace_bytes", "sq_linear_fwd_mx4", "sq_linear_fwd_static")
+SQ_FWD_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class SqW4(ctypes.Structure):
@@ -104,6 +105,8 @@ def lib() -> ctypes.CDLL:
         L.sq_linear_dgrad.argtypes = [vp, i64, ctypes.POINTER(SqW4), vp, ctypes.c_int, vp,
                                       ctypes.c_size_t, vp]
         L.sq_linear_dgrad.restype = ctypes.c_int
+        L.sq_linear_fwd_static.argtypes = [vp, i64, ctypes.POINTER(SqW4), vp, ctypes.c_int, vp]
+        L.sq_linear_fwd_static.restype = ctypes.c_int
         L.sq_reconstruct_bf16.argtypes = [ctypes.POINTER(SqW4), vp, vp]
         L.sq_reconstruct_bf16.restype = ctypes.c_int
         P8 = ctypes.POINTER(SqW8)
@@ -166,6 +169,10 @@ def sq_linear_fwd_contract(m: int, p: SqW4, y, y_dtype: int, workspace, workspac
                            stream) -> int:
     return lib().sq_linear_fwd_contract(m, ctypes.byref(p), y, y_dtype, workspace,
                                         workspace_bytes, stream)
+
+
+def sq_linear_fwd_static(x, m: int, p: SqW4, y, y_dtype: int, stream) -> int:
+    return lib().sq_linear_fwd_static(x, m, ctypes.byref(p), y, y_dtype, stream)
 
 
 def sq_reconstruct_bf16(p: SqW4, w_hat, stream) -> int:

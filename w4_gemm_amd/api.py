@@ -126,6 +126,22 @@ def linear_fwd(x: torch.Tensor, p: W4Payload, out_dtype=torch.float32,
     return out
 
 
+def linear_fwd_static(x: torch.Tensor, p: W4Payload, out_dtype=torch.float32,
+                      out: torch.Tensor | None = None):
+    """sq_linear_fwd_static: the forward with the library's static scratch (no workspace)."""
+    _require(x, torch.bfloat16, "x")
+    m = S.check_rows("x", x.shape, p.k)
+    if out is None:
+        out = torch.empty((m, p.n), dtype=out_dtype, device=x.device)
+    _require(out, out.dtype, "out")
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (m, p.n):
+        raise ValueError("out must be fp32 or bf16 of shape [M, N]")
+    dt = SQ_BF16 if out.dtype == torch.bfloat16 else SQ_F32
+    _check(_lib.sq_linear_fwd_static(x.data_ptr(), m, p.abi(), out.data_ptr(), dt, _stream()),
+           "sq_linear_fwd_static")
+    return out
+
+
 def linear_fwd_rotate(x: torch.Tensor, p: W4Payload, workspace: torch.Tensor):
     """sq_linear_fwd_rotate: the activation half of the forward, into `workspace`."""
     _require(x, torch.bfloat16, "x")

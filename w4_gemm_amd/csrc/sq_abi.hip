@@ -69,6 +69,27 @@ sq_status_t check_payload_mx(const sq_mx4_t* p) {
 
 sq_status_t from_hip(hipError_t e) { return e == hipSuccess ? SQ_OK : SQ_E_HIP; }
 
+// Scratch of the allocation-free forward: one copy per device, part of the
+// code object's zero-initialised data, held until the process ends.  In host
+// code its name is a host-side stand-in; the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[SQ_FWD_STATIC_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+sq_status_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SQ_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SQ_E_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +200,29 @@ sq_status_t sq_linear_fwd(const uint16_t* x, int64_t m, const sq_w4_t* p, void* 
     return st;
   return from_hip(sq::launch_fwd_contract(plan, p->codes, p->scales, p->lora_up, y,
                                           y_dtype == SQ_BF16, workspace, s));
+}
+
+sq_status_t sq_linear_fwd_static(const uint16_t* x, int64_t m, const sq_w4_t* p, void* y,
+                                 sq_dtype_t y_dtype, void* stream) {
+  if (y_dtype != SQ_F32 && y_dtype != SQ_BF16) return SQ_E_DTYPE;
+  sq_status_t st = check_payload(p, true);
+  if (st != SQ_OK) return st;
+  if (m < 0) return SQ_E_SHAPE;
+  if (m == 0) return SQ_OK;
+  if (!x || !y) return SQ_E_NULL;
+  if (!aligned16(x) || !aligned16(y)) return SQ_E_ALIGN;
+  const sq::FwdPlan plan = make_fwd_plan(m, p);
+  if (plan.total > SQ_FWD_STATIC_SCRATCH_BYTES) return SQ_E_WORKSPACE;
+  if ((st = check_device()) != SQ_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != SQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (plan.dec)
+    return from_hip(sq::launch_decode_contract(plan, x, p->lora_down, p->codes, p->scales,
+                                               p->lora_up, y, y_dtype == SQ_BF16, ws, s));
+  if ((st = from_hip(sq::launch_fwd_rotate(plan, x, p->lora_down, ws, s))) != SQ_OK) return st;
+  return from_hip(sq::launch_fwd_contract(plan, p->codes, p->scales, p->lora_up, y,
+                                          y_dtype == SQ_BF16, ws, s));
 }
 
 size_t sq_linear_dgrad_workspace_bytes(int64_t m, const sq_w4_t* p) {
