@@ -7,9 +7,11 @@ already resident in HBM:
   sq_linear_fwd      (rotation pre-phase + fused int4 contraction),
   sq_reconstruct_bf16 (bf16 W_hat from the payload).
 Each entry point is timed on its own with HIP events on the stream it runs
-on (torch's current stream), after warm-up calls; the reconstruct rotates
-over three payload/output sets so the 256 MB Infinity Cache cannot serve its
-reads.  The headline `value` is the fused forward's TFLOP/s at
+on (torch's current stream), after warm-up calls.  Every timed loop cycles
+through distinct input/output sets of at least 512 MB in total (two whole
+forward sets of payload, x, y and workspace; enough payload copies for the
+small-M graphs; three reconstruct sets; two quantizer inputs), so the 256 MB
+Infinity Cache cannot serve the next call from the previous one.  The headline `value` is the fused forward's TFLOP/s at
 4480x16384x6144 (flops = 2MNK + 2Mr(N+K)); reconstruct GB/s and quantize
 GB/s are reported beside it.
 
@@ -90,6 +92,68 @@ def measured_traffic(path, src):
         return None
 
 
+def sets_for(set_bytes, rotate_mb):
+    """How many distinct sets of `set_bytes` make at least `rotate_mb` MB (at least 2)."""
+    return max(2, int(np.ceil(rotate_mb * 1e6 / max(set_bytes, 1.0))))
+
+
+def split(torch, w, rank, seed=0):
+    """bf16 rank-`rank` factors (up [N, r], down [K, r]) of a device weight through
+    the builder's seeded fp64 randomized split."""
+    from w4_gemm_amd import builder as B
+    from w4_gemm_amd.svd_init import _bf16_from_f64
+    g = torch.Generator(device=w.device).manual_seed(seed)
+    u, s, v = B.randomized_split(torch, w.double(), rank, g)
+    rs = s[:rank].sqrt()
+    up = _bf16_from_f64((u[:, :rank] * rs).cpu().numpy()).to(w.device)
+    down = _bf16_from_f64((v[:, :rank] * rs).cpu().numpy()).to(w.device)
+    return up, down
+
+
+def clone_payload(W, p):
+    """A distinct copy of a W4 payload (codes, scales and both factors)."""
+    return W.W4Payload(p.codes.clone(), p.scales.clone(),
+                       None if p.up is None else p.up.clone(),
+                       None if p.down is None else p.down.clone(), p.group)
+
+
+SETTLE_S = 0.1
+
+
+def settle(torch, fn, seconds=SETTLE_S):
+    """Run fn(i) back to back for `seconds` of wall time before a timed loop.
+
+    After the GPU idles (setup, host work between measurements) its clock
+    ramps back up over the first few milliseconds of load, and the very first
+    heavy burst of a process has shown one stall of tens of milliseconds;
+    the timed steps measure the steady state that follows."""
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        fn(i)
+        i += 1
+        if i % 4 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                return
+
+
+def event_times(torch, fn, steps, warmup):
+    """Per-call milliseconds of fn(i) for i = 0..steps-1, HIP events on the
+    current stream, after the clock settles and `warmup` untimed calls."""
+    settle(torch, fn)
+    for i in range(warmup):
+        fn(i)
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for i, (a, b) in enumerate(marks):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in marks])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +165,8 @@ def main():
     ap.add_argument("--ops",
                     default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs,w8,mx,bf16gemm")
     ap.add_argument("--small-m", default="1,16,128")
+    ap.add_argument("--rotate-mb", type=float, default=512.0,
+                    help="least total size of the distinct sets a timed loop cycles through")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only; the layer shards by output rows "
@@ -128,21 +194,21 @@ def main():
     w = torch.from_numpy(w_np).to(dev)
     x = torch.from_numpy(x_np.view(np.int16)).view(torch.bfloat16).to(dev)
     del w_np
-    # host prerequisite: rank-R factors.  A randomized range finder stands in for
-    # the full fp64 SVD here (same shapes and magnitudes; kernel cost does not
-    # depend on the factor values).
-    torch.manual_seed(0)
-    u, s, v = torch.svd_lowrank(w, q=R + 8, niter=2)
-    rs = s[:R].sqrt()
-    up = (u[:, :R] * rs).to(torch.bfloat16).contiguous()
-    down = (v[:, :R] * rs).to(torch.bfloat16).contiguous()
-    del u, s, v
+    # host prerequisite: rank-R factors, from the builder's seeded fp64
+    # randomized split (within 1e-4 of the exact SVD's residual energy)
+    up, down = split(torch, w, R)
     p0, fidx, flags = W.quantize_weight(w, up, down, G)
     torch.cuda.synchronize()
     assert int(flags[0]) == 0, "quantizer flagged the synthetic weight"
-    payloads = [p0] + [W.W4Payload(p0.codes.clone(), p0.scales.clone(), up, down, G) for _ in range(2)]
-    ws = torch.empty(W.fwd_workspace_bytes(M, p0), dtype=torch.uint8, device=dev)
-    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    payloads = [p0] + [clone_payload(W, p0) for _ in range(2)]
+    pay_bytes = N * K / 2 + N * (K // G) * 2 + (N + K) * R * 2
+    # forward sets: payload, x, y (bf16) and workspace each
+    fset_bytes = pay_bytes + M * K * 2 + M * N * 2 + W.fwd_workspace_bytes(M, p0)
+    nf = sets_for(fset_bytes, args.rotate_mb)
+    xs = [x] + [x.clone() for _ in range(nf - 1)]
+    fpays = payloads[:nf] + [clone_payload(W, p0) for _ in range(nf - len(payloads[:nf]))]
+    wss = [torch.empty(W.fwd_workspace_bytes(M, p0), dtype=torch.uint8, device=dev) for _ in range(nf)]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(nf)]
     what = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(3)]
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
@@ -155,68 +221,51 @@ def main():
     t0 = time.time()
     # ---------------------------------------------------------------- forward
     if "fwd" in ops:
-        for _ in range(args.warmup):
-            W.linear_fwd_rotate(x, p0, ws)
-            W.linear_fwd_contract(M, p0, y, ws)
+        settle(torch, lambda i: (W.linear_fwd_rotate(xs[i % nf], fpays[i % nf], wss[i % nf]),
+                                 W.linear_fwd_contract(M, fpays[i % nf], ys[i % nf], wss[i % nf])))
+        for i in range(args.warmup):
+            W.linear_fwd_rotate(xs[i % nf], fpays[i % nf], wss[i % nf])
+            W.linear_fwd_contract(M, fpays[i % nf], ys[i % nf], wss[i % nf])
         marks = [(ev(), ev(), ev()) for _ in range(args.steps)]
-        for a, b, c in marks:
+        for i, (a, b, c) in enumerate(marks):
+            j = i % nf
             a.record()
-            W.linear_fwd_rotate(x, p0, ws)
+            W.linear_fwd_rotate(xs[j], fpays[j], wss[j])
             b.record()
-            W.linear_fwd_contract(M, p0, y, ws)
+            W.linear_fwd_contract(M, fpays[j], ys[j], wss[j])
             c.record()
         torch.cuda.synchronize()
         rot = np.array([a.elapsed_time(b) for a, b, _ in marks])
         con = np.array([b.elapsed_time(c) for _, b, c in marks])
         res["fwd"] = (rot + con, rot, con)
+        res["fwd_sets"] = (nf, fset_bytes * nf)
+        # the shader clock while a burst of forwards runs (the idle level differs)
+        for i in range(12):
+            W.linear_fwd_rotate(xs[i % nf], fpays[i % nf], wss[i % nf])
+            W.linear_fwd_contract(M, fpays[i % nf], ys[i % nf], wss[i % nf])
+        time.sleep(0.004)
+        res["clock_under_load"] = read_clocks()
+        torch.cuda.synchronize()
     # ---------------------------------------------------------------- reconstruct
     if "reconstruct" in ops:
-        for i in range(args.warmup):
-            W.reconstruct_bf16(payloads[i % 3], out=what[i % 3])
-        marks = [(ev(), ev()) for _ in range(args.steps)]
-        for i, (a, b) in enumerate(marks):
-            a.record()
-            W.reconstruct_bf16(payloads[i % 3], out=what[i % 3])
-            b.record()
-        torch.cuda.synchronize()
-        res["reconstruct"] = np.array([a.elapsed_time(b) for a, b in marks])
+        res["reconstruct"] = event_times(
+            torch, lambda i: W.reconstruct_bf16(payloads[i % 3], out=what[i % 3]), args.steps,
+            args.warmup)
     # ---------------------------------------------------------------- input gradient
     if "dgrad" in ops:
         gen = torch.Generator(device=dev).manual_seed(0)
         dy = torch.randn((M, N), generator=gen, device=dev).to(torch.bfloat16)
         dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         dws = torch.empty(W.dgrad_workspace_bytes(M, p0), dtype=torch.uint8, device=dev)
-        for _ in range(args.warmup):
-            W.linear_dgrad(dy, p0, out=dx, workspace=dws)
-        marks = [(ev(), ev()) for _ in range(args.steps)]
-        for a, b in marks:
-            a.record()
-            W.linear_dgrad(dy, p0, out=dx, workspace=dws)
-            b.record()
-        torch.cuda.synchronize()
-        res["dgrad"] = np.array([a.elapsed_time(b) for a, b in marks])
+        dps = [p0, payloads[1]]
+        res["dgrad"] = event_times(
+            torch, lambda i: W.linear_dgrad(dy, dps[i % 2], out=dx, workspace=dws), args.steps,
+            args.warmup)
         del dy, dx, dws
     # ---------------------------------------------------------------- quantize
     if "quantize" in ops:
-        qp = W.empty_payload(N, K, G, R, dev)
-        qp.up, qp.down = up, down
-        qf = torch.empty((N, K // G), dtype=torch.uint8, device=dev)
-        qflags = torch.zeros(4, dtype=torch.int32, device=dev)
-        from w4_gemm_amd import _lib
-        stream = torch.cuda.current_stream().cuda_stream
-
-        def quant():
-            st = _lib.sq_quantize_weight(w.data_ptr(), qp.abi(), qf.data_ptr(), qflags.data_ptr(), stream)
-            assert st == 0, st
-        for _ in range(args.warmup):
-            quant()
-        marks = [(ev(), ev()) for _ in range(args.steps)]
-        for a, b in marks:
-            a.record()
-            quant()
-            b.record()
-        torch.cuda.synchronize()
-        res["quantize"] = np.array([a.elapsed_time(b) for a, b in marks])
+        res["quantize"] = quantize_times(torch, W, dev, [w, w.clone()], up, down, G, args.steps,
+                                         args.warmup)
     # ---------------------------------------------------------------- int8-residual mode
     if "w8" in ops:
         res["w8"] = w8_run(torch, W, dev, w, x, what, M, N, K, args.steps, args.warmup)
@@ -231,19 +280,18 @@ def main():
         res["builder"] = builder_run(torch, dev)
     # ---------------------------------------------------------------- other shapes
     if "configs" in ops:
-        res["configs"] = other_configs(torch, W, dev, [2, 3, 5], max(5, args.steps // 5),
-                                       args.warmup)
+        res["configs"] = other_configs(torch, W, dev, [1, 2, 3, 5], max(5, args.steps // 5),
+                                       args.warmup, args.rotate_mb)
     # ---------------------------------------------------------------- small-M sweep
     if "smallm" in ops and args.small_m:
         res["smallm"] = small_m_sweep(torch, W, dev, [int(v) for v in args.small_m.split(",")],
-                                      args.steps, args.warmup)
+                                      args.steps, args.warmup, args.rotate_mb)
     torch.cuda.synchronize()
     wall = time.time() - t0
 
     # ---------------------------------------------------------------- metrics
     flops_fwd = 2.0 * M * N * K + 2.0 * M * R * (N + K)
     flops_gemm = 2.0 * M * N * K + 2.0 * M * N * R
-    pay_bytes = N * K / 2 + N * (K // G) * 2 + (N + K) * R * 2
     rec_bytes = pay_bytes + 2.0 * N * K
     quant_bytes = 4.0 * N * K + N * K / 2 + N * (K // G) * 3 + (N + K) * R * 2
     out = {}
@@ -257,6 +305,7 @@ def main():
                    fwd_ms_p90=float(np.percentile(tot, 90)), fwd_rotate_ms=t_rot,
                    fwd_contract_ms=t_con, fwd_tflops=flops_fwd / (t_fwd * 1e-3) / 1e12)
         out["fwd_pct_bf16_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_F16_TFLOPS
+        out["fwd_rotating_sets"] = {"sets": res["fwd_sets"][0], "bytes": res["fwd_sets"][1]}
         # rotation half: reads x twice, writes xh (fp16); the t / stats side buffers are small
         rot_bytes = 3.0 * M * K * 2
         out["fwd_rotate_gbps"] = rot_bytes / (t_rot * 1e-3) / 1e9
@@ -274,7 +323,7 @@ def main():
                    reconstruct_gbps=rec_bytes / (t * 1e-3) / 1e9)
         out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
     if "quantize" in res:
-        t = float(np.mean(res["quantize"]))
+        t = float(np.mean(res["quantize"]["times"]))
         ms_step += t
         out.update(quantize_ms=t, quantize_gbps=quant_bytes / (t * 1e-3) / 1e9)
         out["quantize_pct_hbm_peak"] = 100.0 * out["quantize_gbps"] / PEAK_HBM_GBPS
@@ -285,6 +334,7 @@ def main():
         out["quantize_alu"] = {"bound": "alu", "achieved": alu / 1e12, "peak": PEAK_VALU_TOPS,
                                "unit": "Tlane-op/s", "frac": alu / 1e12 / PEAK_VALU_TOPS,
                                "ops_per_element": SWEEP_OPS_PER_ELEMENT}
+        out["quantize_other_configs"] = res["quantize"]["other"]
     if "dgrad" in res:
         t = float(np.mean(res["dgrad"]))
         out.update(dgrad_ms=t, dgrad_ms_median=float(np.median(res["dgrad"])),
@@ -323,9 +373,12 @@ def main():
     }
     line.update({k: v for k, v in out.items()})
     line["timed_wall_s"] = wall
+    line["settle_s_per_timed_loop"] = SETTLE_S
     line["setup_s"] = t_setup
     line["device"] = torch.cuda.get_device_name(0)
     line["clocks"] = read_clocks()
+    if "clock_under_load" in res:
+        line["clocks_under_load"] = res["clock_under_load"]
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p0, x, cfg, args.cpu_rows)
@@ -340,12 +393,7 @@ def w8_run(torch, W, dev, w, x, what, M, N, K, steps, warmup):
     call: rotation pre-phase + int8 contraction) and sq_reconstruct_bf16_w8
     (rotating over three payload/output sets), each timed with HIP events."""
     R = 16
-    torch.manual_seed(0)
-    u, s, v = torch.svd_lowrank(w, q=R + 8, niter=2)
-    rs = s[:R].sqrt()
-    up = (u[:, :R] * rs).to(torch.bfloat16).contiguous()
-    down = (v[:, :R] * rs).to(torch.bfloat16).contiguous()
-    del u, s, v
+    up, down = split(torch, w, R)
     qws = torch.empty(W._lib.sq_quantize_weight_w8_workspace_bytes(W.empty_payload_w8(N, K, R, dev).abi()),
                       dtype=torch.uint8, device=dev)
     p0, fidx, flags = W.quantize_weight_w8(w, up, down, workspace=qws)
@@ -359,17 +407,11 @@ def w8_run(torch, W, dev, w, x, what, M, N, K, steps, warmup):
         return torch.cuda.Event(enable_timing=True)
 
     def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        marks = [(ev(), ev()) for _ in range(steps)]
-        for i, (a, b) in enumerate(marks):
-            a.record()
-            fn(i)
-            b.record()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in marks]))
+        return float(np.mean(event_times(torch, fn, steps, warmup)))
 
-    t_fwd = timed(lambda i: W.linear_fwd_w8(x, p0, out=y, workspace=ws))
+    y2, x2 = torch.empty_like(y), x.clone()
+    t_fwd = timed(lambda i: W.linear_fwd_w8(x if i % 2 else x2, pays[i % 3], out=y if i % 2 else y2,
+                                            workspace=ws))
     t_rec = timed(lambda i: W.reconstruct_bf16_w8(pays[i % 3], out=what[i % 3]))
     t_q = timed(lambda i: W.quantize_weight_w8(w, up, down, want_fidx=False, workspace=qws))
     flops = 2.0 * M * N * K + 2.0 * M * R * (N + K)
@@ -380,11 +422,15 @@ def w8_run(torch, W, dev, w, x, what, M, N, K, steps, warmup):
            "quantize_ms": t_q}
     out["fwd_pct_bf16_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_F16_TFLOPS
     out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
+    npay = sets_for(pay, 512.0)
+    spays = pays[:npay] + [W.W8Payload(p0.codes.clone(), p0.scales.clone(), up, down)
+                           for _ in range(npay - len(pays[:npay]))]
     out["fwd_small_m"] = small_m_modes(
         torch, dev, x, N, K, pay, steps, warmup,
         lambda m: W.fwd_w8_workspace_bytes(m, p0),
-        lambda xx, yy, wss: W.linear_fwd_w8(xx, p0, out=yy, workspace=wss))
-    del pays, p0, qws, ws, y
+        lambda i, xx, yy, wss: W.linear_fwd_w8(xx, spays[i % npay], out=yy, workspace=wss))
+    out["fwd_small_m"]["payload_copies"] = npay
+    del pays, spays, p0, qws, ws, y, y2, x2
     torch.cuda.empty_cache()
     return out
 
@@ -407,17 +453,11 @@ def mx_run(torch, W, dev, w, x, up, down, what, M, N, K, steps, warmup):
         return torch.cuda.Event(enable_timing=True)
 
     def timed(fn):
-        for i in range(warmup):
-            fn(i)
-        marks = [(ev(), ev()) for _ in range(steps)]
-        for i, (a, b) in enumerate(marks):
-            a.record()
-            fn(i)
-            b.record()
-        torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in marks]))
+        return float(np.mean(event_times(torch, fn, steps, warmup)))
 
-    t_fwd = timed(lambda i: W.linear_fwd_mx4(x, p0, out=y, workspace=ws))
+    y2, x2 = torch.empty_like(y), x.clone()
+    t_fwd = timed(lambda i: W.linear_fwd_mx4(x if i % 2 else x2, pays[i % 3], out=y if i % 2 else y2,
+                                             workspace=ws))
     t_rec = timed(lambda i: W.reconstruct_bf16_mx4(pays[i % 3], out=what[i % 3]))
     t_q = timed(lambda i: W.quantize_weight_mx4(w, up, down))
     flops = 2.0 * M * N * K + 2.0 * M * R * (N + K)
@@ -428,31 +468,36 @@ def mx_run(torch, W, dev, w, x, up, down, what, M, N, K, steps, warmup):
            "quantize_ms": t_q}
     out["fwd_pct_fp4_mfma_peak"] = 100.0 * out["fwd_tflops"] / PEAK_FP4_TFLOPS
     out["reconstruct_pct_hbm_peak"] = 100.0 * out["reconstruct_gbps"] / PEAK_HBM_GBPS
+    npay = sets_for(pay, 512.0)
+    spays = pays[:npay] + [W.MX4Payload(p0.codes.clone(), p0.exps.clone(), up, down)
+                           for _ in range(npay - len(pays[:npay]))]
     out["fwd_small_m"] = small_m_modes(
         torch, dev, x, N, K, pay, steps, warmup,
         lambda m: W.fwd_mx4_workspace_bytes(m, p0),
-        lambda xx, yy, wss: W.linear_fwd_mx4(xx, p0, out=yy, workspace=wss))
-    del pays, p0, ws, y
+        lambda i, xx, yy, wss: W.linear_fwd_mx4(xx, spays[i % npay], out=yy, workspace=wss))
+    out["fwd_small_m"]["payload_copies"] = npay
+    del pays, spays, p0, ws, y, y2, x2
     torch.cuda.empty_cache()
     return out
 
 
 def graph_us(torch, fn, steps, warmup):
-    """GPU time per call of fn(), in microseconds, from one replay of a HIP
-    graph of `steps` back-to-back calls (small calls finish faster than the
-    host enqueues them, so eager timing would measure the host)."""
-    for _ in range(warmup):
-        fn()
+    """GPU time per call of fn(i), in microseconds, from one replay of a HIP
+    graph of `steps` back-to-back calls i = 0..steps-1 (small calls finish
+    faster than the host enqueues them, so eager timing would measure the
+    host)."""
+    settle(torch, fn)
+    for i in range(warmup):
+        fn(i)
     side = torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=side):
-            for _ in range(steps):
-                fn()
+            for i in range(steps):
+                fn(i)
     torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
+    settle(torch, lambda i: graph.replay())
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     graph.replay()
@@ -463,13 +508,14 @@ def graph_us(torch, fn, steps, warmup):
 
 def small_m_modes(torch, dev, x, N, K, pay, steps, warmup, ws_bytes, fwd, ms=(1, 16, 128)):
     """Forward of the int8 or MXFP4 payload at small M (first M rows of the
-    layer's activations), graph-replayed; GB/s of payload + x + y."""
+    layer's activations), graph-replayed with consecutive calls on distinct
+    payload copies; GB/s of payload + x + y."""
     out = {}
     for m in ms:
         xm = x[:m].contiguous()
         y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(ws_bytes(m), dtype=torch.uint8, device=dev)
-        t = graph_us(torch, lambda: fwd(xm, y, ws), steps, warmup)
+        t = graph_us(torch, lambda i: fwd(i, xm, y, ws), steps, warmup)
         by = pay + m * K * 2 + m * N * 2
         out[str(m)] = {"us": t, "gbps": by / (t * 1e-6) / 1e9,
                        "pct_hbm_peak": 100.0 * by / (t * 1e-6) / 1e9 / PEAK_HBM_GBPS}
@@ -530,88 +576,135 @@ def builder_run(torch, dev):
         shutil.rmtree(tmp, ignore_errors=True)
 
 
-def layer(torch, W, dev, cfg_id):
+def layer(torch, W, dev, cfg_id, with_w=False):
     """Synthetic layer of a configuration: its payload (quantized on the GPU
-    with randomized rank-R factors) and its activation draw (numpy bf16)."""
+    with the seeded rank-R split) and its activation draw (numpy bf16)."""
     from synth import CONFIGS, gen_activations, gen_weight
     cfg = CONFIGS[cfg_id]
     rng = np.random.default_rng(0)
     w = torch.from_numpy(gen_weight(rng, cfg.N, cfg.K, cfg.spike)).to(dev)
     x_all = gen_activations(rng, cfg.M, cfg.K, cfg.outlier_frac)
-    torch.manual_seed(0)
-    u, s, v = torch.svd_lowrank(w, q=cfg.rank + 8, niter=2)
-    rs = s[:cfg.rank].sqrt()
-    up = (u[:, :cfg.rank] * rs).to(torch.bfloat16).contiguous()
-    down = (v[:, :cfg.rank] * rs).to(torch.bfloat16).contiguous()
+    up, down = split(torch, w, cfg.rank)
     p, _, flags = W.quantize_weight(w, up, down, cfg.group)
     torch.cuda.synchronize()
     assert int(flags[0]) == 0
-    return cfg, p, x_all
+    return (cfg, p, x_all, w) if with_w else (cfg, p, x_all)
 
 
-def other_configs(torch, W, dev, ids, steps, warmup):
-    """The whole forward at the other layer shapes (their own M), timed per
-    call with HIP events on the current stream."""
+def quantize_times(torch, W, dev, ws_in, up, down, G, steps, warmup):
+    """sq_quantize_weight on the headline weight (cycling through the given
+    copies of it) and, as extra rows, on the fused-QKV weight (9216 x 3072
+    g64) and the tiny layer, each cycling through >= 512 MB of inputs."""
+    from w4_gemm_amd import _lib
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def runner(wl, upl, dnl, group):
+        n, k = wl[0].shape
+        qp = W.empty_payload(n, k, group, upl.shape[1], dev)
+        qp.up, qp.down = upl, dnl
+        abi = qp.abi()
+        qf = torch.empty((n, k // group), dtype=torch.uint8, device=dev)
+        flags = torch.zeros(4, dtype=torch.int32, device=dev)
+
+        def go(i):
+            st = _lib.sq_quantize_weight(wl[i % len(wl)].data_ptr(), abi, qf.data_ptr(),
+                                         flags.data_ptr(), stream)
+            assert st == 0, st
+        return go
+
+    times = event_times(torch, runner(ws_in, up, down, G), steps, warmup)
+    other = {}
+    from synth import CONFIGS, gen_weight
+    for cid in (3, 1):
+        cfg = CONFIGS[cid]
+        w = torch.from_numpy(gen_weight(np.random.default_rng(0), cfg.N, cfg.K, cfg.spike)).to(dev)
+        u, d = split(torch, w, cfg.rank)
+        nb = 4.0 * cfg.N * cfg.K + cfg.N * cfg.K / 2 + cfg.N * (cfg.K // cfg.group) * 3 + \
+            (cfg.N + cfg.K) * cfg.rank * 2
+        wl = [w] + [w.clone() for _ in range(sets_for(nb, 512.0) - 1)]
+        t = float(np.mean(event_times(torch, runner(wl, u, d, cfg.group), steps, warmup)))
+        other[cfg.name] = {"us": t * 1e3, "gbps": nb / (t * 1e-3) / 1e9,
+                           "pct_hbm_peak": 100.0 * nb / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                           "rotating_sets": len(wl)}
+        del wl, w
+    torch.cuda.empty_cache()
+    return {"times": times, "other": other}
+
+
+def other_configs(torch, W, dev, ids, steps, warmup, rotate_mb):
+    """The whole forward at the other layer shapes (their own M), and the
+    reconstruct at the shapes whose text names it (attention projection,
+    MLP-down, tiny), timed per call with HIP events on the current stream,
+    each loop cycling through >= rotate_mb MB of distinct sets."""
     out = {}
     for cid in ids:
         cfg, p, x_all = layer(torch, W, dev, cid)
-        M, N, K, R = cfg.M, cfg.N, cfg.K, cfg.rank
-        x = torch.from_numpy(x_all.view(np.int16)).view(torch.bfloat16).to(dev)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(W.fwd_workspace_bytes(M, p), dtype=torch.uint8, device=dev)
-        for _ in range(warmup):
-            W.linear_fwd(x, p, out=y, workspace=ws)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for a, b in evs:
-            a.record()
-            W.linear_fwd(x, p, out=y, workspace=ws)
-            b.record()
-        torch.cuda.synchronize()
-        t = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        M, N, K, G, R = cfg.M, cfg.N, cfg.K, cfg.group, cfg.rank
+        pay = N * K / 2 + N * (K // G) * 2 + (N + K) * R * 2
+        fb = pay + M * K * 2 + M * N * 2 + W.fwd_workspace_bytes(M, p)
+        nf = sets_for(fb, rotate_mb)
+        pays = [p] + [clone_payload(W, p) for _ in range(nf - 1)]
+        x0 = torch.from_numpy(x_all.view(np.int16)).view(torch.bfloat16).to(dev)
+        xs = [x0] + [x0.clone() for _ in range(nf - 1)]
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(nf)]
+        wss = [torch.empty(W.fwd_workspace_bytes(M, p), dtype=torch.uint8, device=dev)
+               for _ in range(nf)]
+        t = float(np.median(event_times(
+            torch, lambda i: W.linear_fwd(xs[i % nf], pays[i % nf], out=ys[i % nf],
+                                          workspace=wss[i % nf]), steps, warmup)))
         fl = 2.0 * M * N * K + 2.0 * M * R * (N + K)
-        out[cfg.name] = {"us": t * 1e3, "tflops": fl / (t * 1e-3) / 1e12,
-                         "pct_mfma_peak": 100.0 * fl / (t * 1e-3) / 1e12 / PEAK_F16_TFLOPS}
-        del p, x, y, ws
+        row = {"us": t * 1e3, "tflops": fl / (t * 1e-3) / 1e12,
+               "pct_mfma_peak": 100.0 * fl / (t * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+               "rotating_sets": nf}
+        del xs, ys, wss
+        if cid in (1, 2, 5):
+            rb = pay + 2.0 * N * K
+            nr = sets_for(rb, rotate_mb)
+            rp = pays[:nr] + [clone_payload(W, p) for _ in range(nr - len(pays[:nr]))]
+            outs = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in range(nr)]
+            tr = float(np.mean(event_times(
+                torch, lambda i: W.reconstruct_bf16(rp[i % nr], out=outs[i % nr]), steps, warmup)))
+            row["reconstruct"] = {"us": tr * 1e3, "gbps": rb / (tr * 1e-3) / 1e9,
+                                  "pct_hbm_peak": 100.0 * rb / (tr * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                  "rotating_sets": nr}
+            del rp, outs
+        out[cfg.name] = row
+        del p, pays
+        torch.cuda.empty_cache()
     return out
 
 
-def small_m_sweep(torch, W, dev, ms, steps, warmup):
+def small_m_sweep(torch, W, dev, ms, steps, warmup, rotate_mb=512.0):
     """Forward at small M on the 6144x16384 g32 rank-32 weight, HBM-bound:
     GB/s of the bytes one call must move (payload + x + y), first M rows of
     the M=4480 activation draw.  At these sizes one call's kernels run for
     less time than the host needs to enqueue them, so the calls are captured
     once in a HIP graph and the graph is replayed: the figure is GPU time
-    per call (`us`), with the eager per-call time beside it (`eager_us`)."""
+    per call (`us`), with the eager per-call time beside it (`eager_us`).
+    Consecutive calls use distinct payload copies (>= rotate_mb MB in all),
+    so no call finds its payload in the Infinity Cache."""
     cfg, p, x_all = layer(torch, W, dev, 5)
     N, K, G, R = cfg.N, cfg.K, cfg.group, cfg.rank
     pay = N * K / 2 + N * (K // G) * 2 + (N + K) * R * 2
-    out = {}
+    npay = sets_for(pay, rotate_mb)
+    pays = [p] + [clone_payload(W, p) for _ in range(npay - 1)]
+    out = {"payload_copies": npay}
     for m in ms:
         x = torch.from_numpy(x_all[:m].view(np.int16).copy()).view(torch.bfloat16).to(dev)
         y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(W.fwd_workspace_bytes(m, p), dtype=torch.uint8, device=dev)
-        for _ in range(warmup):
-            W.linear_fwd(x, p, out=y, workspace=ws)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for a, b in evs:
-            a.record()
-            W.linear_fwd(x, p, out=y, workspace=ws)
-            b.record()
-        torch.cuda.synchronize()
-        eager = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        eager = float(np.median(event_times(
+            torch, lambda i: W.linear_fwd(x, pays[i % npay], out=y, workspace=ws), steps, warmup)))
         # graph: `steps` calls captured back to back on a side stream
         side = torch.cuda.Stream()
         torch.cuda.synchronize()
         with torch.cuda.stream(side):
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph, stream=side):
-                for _ in range(steps):
-                    W.linear_fwd(x, p, out=y, workspace=ws)
+                for i in range(steps):
+                    W.linear_fwd(x, pays[i % npay], out=y, workspace=ws)
         torch.cuda.synchronize()
-        graph.replay()
-        torch.cuda.synchronize()
+        settle(torch, lambda i: graph.replay())
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         graph.replay()
@@ -622,6 +715,8 @@ def small_m_sweep(torch, W, dev, ms, steps, warmup):
         out[str(m)] = {"us": t * 1e3, "eager_us": eager * 1e3, "gbps": by / (t * 1e-3) / 1e9,
                        "pct_hbm_peak": 100.0 * by / (t * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                        "tflops": (2.0 * m * N * K + 2.0 * m * R * (N + K)) / (t * 1e-3) / 1e12}
+    del pays
+    torch.cuda.empty_cache()
     return out
 
 
@@ -631,16 +726,7 @@ def bf16_gemm_run(torch, dev, w, x, M, N, K, steps, warmup):
     shape; the on-box counterpart of the pages' production bf16 GEMM column."""
     wt = w.t().contiguous().to(torch.bfloat16)   # [K, N], no transposed view
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    for _ in range(warmup):
-        torch.mm(x, wt, out=y)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for a, b in evs:
-        a.record()
-        torch.mm(x, wt, out=y)
-        b.record()
-    torch.cuda.synchronize()
-    t = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    t = float(np.mean(event_times(torch, lambda i: torch.mm(x, wt, out=y), steps, warmup)))
     del wt, y
     torch.cuda.empty_cache()
     return {"ms": t, "tflops": 2.0 * M * N * K / (t * 1e-3) / 1e12}
@@ -694,9 +780,15 @@ def torch_index(sel, t):
 def cpu_baseline(p, x, cfg, rows):
     """The oracle's forward on `rows` sampled rows of x against the full payload."""
     import oracle as O
+    blas = {}
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        if info:
+            blas = {"vendor": info[0].get("internal_api"), "version": info[0].get("version"),
+                    "threading": info[0].get("threading_layer"),
+                    "architecture": info[0].get("architecture")}
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     codes = p.codes.cpu().numpy()
@@ -714,7 +806,8 @@ def cpu_baseline(p, x, cfg, rows):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"oracle.forward (numpy fp64) on {rows} of {cfg.M} rows, full N={cfg.N} "
                       f"K={cfg.K}, including unpack/dequant; {dt:.2f} s",
-            "seconds": dt}
+            "seconds": dt, "blas": blas, "os_cpu_count": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 if __name__ == "__main__":
