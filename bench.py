@@ -117,7 +117,7 @@ def clone_payload(W, p):
                        None if p.down is None else p.down.clone(), p.group)
 
 
-SETTLE_S = 0.1
+SETTLE_S = 0.2
 
 
 def settle(torch, fn, seconds=SETTLE_S):
