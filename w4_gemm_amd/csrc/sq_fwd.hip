@@ -64,11 +64,14 @@ __device__ __forceinline__ void load_x64(uint32_t (&xb)[32], const uint16_t* __r
   }
 }
 
-// Pass 1: grid (ceil(m/16), slices); slice q covers the 256-column blocks
-// [q*bps, q*bps + bps) and the workgroup's four waves take every fourth one.
+// Pass 1: grid (ceil(m / (16 TILES)), slices); slice q covers the
+// 256-column blocks [q*bps, q*bps + bps) and the workgroup's four waves take
+// every fourth one, for TILES 16-row tiles of rows each.  A wave loads its
+// block's downT fragments (the MFMA B operand) once and contracts every row
+// tile against them, so the factor is read from L2 once per TILES tiles.
 // Writes amax_part[q][row] (bf16 magnitude bits; they order like the values)
 // and t_part[q][row][r] (fp32) for the rows below m.
-template <int RANK>
+template <int RANK, int TILES>
 __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ downT, int64_t m, int64_t k,
     int bps, uint32_t* __restrict__ amax_part, float* __restrict__ t_part) {
@@ -78,60 +81,82 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * 16;
-  const int64_t lrow = min(row0 + c, m - 1);   // rows past m read the last row
+  const int64_t rbase = (int64_t)blockIdx.x * 16 * TILES;
   const int64_t nblk = k >> 8, q = blockIdx.y;
   const int64_t b_end = min(nblk, (q + 1) * bps);
 
-  f32x4 acc[RT > 0 ? RT : 1] = {};
-  u16x2 amax2 = {0, 0};
+  f32x4 acc[TILES][RT > 0 ? RT : 1] = {};
+  u16x2 amax2[TILES];
+#pragma unroll
+  for (int tl = 0; tl < TILES; ++tl) amax2[tl] = (u16x2){0, 0};
   for (int64_t b = q * bps + wave; b < b_end; b += PRE_WAVES) {
     // MFMA j contracts columns 32j .. 32j+31 of the block; lane (c, g) holds
     // eight of them, 32j + 8g .. +7, so the four lanes of a row read 64
     // contiguous bytes (of x and of each downT row) per instruction.
     const int64_t col = b * 256 + 8 * g;
-    u32x4 xv[8];
+    bf16x8 bfrag[RT > 0 ? RT : 1][8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xv[j] = *reinterpret_cast<const u32x4*>(x + lrow * k + col + 32 * j);
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, xv[j][e] & 0x7FFF7FFFu));
-    // t: A = x (row c), B = downT (r = 16rt + c), both over the same columns
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8 afrag = __builtin_bit_cast(bf16x8, xv[j]);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const bf16x8 bfrag =
+      for (int j = 0; j < 8; ++j)
+        bfrag[rt][j] =
             *reinterpret_cast<const bf16x8*>(downT + (int64_t)(16 * rt + c) * k + col + 32 * j);
-        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag, acc[rt], 0, 0, 0);
+    // the next tile's x is in flight while one tile is contracted
+    u32x4 xv[2][8];
+    auto load_tile = [&](u32x4 (&dst)[8], int tl) {
+      const int64_t lrow = min(rbase + 16 * tl + c, m - 1);   // rows past m read the last row
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        dst[j] = *reinterpret_cast<const u32x4*>(x + lrow * k + col + 32 * j);
+    };
+    load_tile(xv[0], 0);
+#pragma unroll
+    for (int tl = 0; tl < TILES; ++tl) {
+      if (tl + 1 < TILES) load_tile(xv[(tl + 1) & 1], tl + 1);
+      const u32x4 (&xt)[8] = xv[tl & 1];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          amax2[tl] =
+              __builtin_elementwise_max(amax2[tl], __builtin_bit_cast(u16x2, xt[j][e] & 0x7FFF7FFFu));
+      // t: A = x (row c), B = downT (r = 16rt + c), both over the same columns
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 afrag = __builtin_bit_cast(bf16x8, xt[j]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          acc[tl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[rt][j], acc[tl][rt], 0, 0, 0);
       }
     }
   }
-  // acc[rt][i] = partial t[row0 + 4g + i][16 rt + c]
+  // per row tile: acc[tl][rt][i] = partial t[rbase + 16 tl + 4g + i][16 rt + c]
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int tl = 0; tl < TILES; ++tl) {
+    const int64_t row0 = rbase + 16 * tl;
+    if (tl > 0) __syncthreads();   // the previous tile's sums have been read
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red_t[wave][4 * g + i][16 * rt + c] = acc[rt][i];
-  red_max[wave][lane] = max((uint32_t)amax2[0], (uint32_t)amax2[1]);
-  __syncthreads();
-  for (int i = tid; i < 16 * RANK; i += 64 * PRE_WAVES) {
-    const int rr = i / RANK, r = i - rr * RANK;
-    if (row0 + rr >= m) continue;
-    float t = 0.0f;
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int w = 0; w < PRE_WAVES; ++w) t += red_t[w][rr][r];
-    t_part[(q * m + row0 + rr) * RANK + r] = t;
-  }
-  if (tid < 16 && row0 + tid < m) {
-    uint32_t mx = 0;
+      for (int i = 0; i < 4; ++i) red_t[wave][4 * g + i][16 * rt + c] = acc[tl][rt][i];
+    red_max[wave][lane] = max((uint32_t)amax2[tl][0], (uint32_t)amax2[tl][1]);
+    __syncthreads();
+    for (int i = tid; i < 16 * RANK; i += 64 * PRE_WAVES) {
+      const int rr = i / RANK, r = i - rr * RANK;
+      if (row0 + rr >= m) continue;
+      float t = 0.0f;
 #pragma unroll
-    for (int w = 0; w < PRE_WAVES; ++w)
+      for (int w = 0; w < PRE_WAVES; ++w) t += red_t[w][rr][r];
+      t_part[(q * m + row0 + rr) * RANK + r] = t;
+    }
+    if (tid < 16 && row0 + tid < m) {
+      uint32_t mx = 0;
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) mx = max(mx, red_max[w][tid + 16 * gg]);
-    amax_part[q * m + row0 + tid] = mx;
+      for (int w = 0; w < PRE_WAVES; ++w)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) mx = max(mx, red_max[w][tid + 16 * gg]);
+      amax_part[q * m + row0 + tid] = mx;
+    }
   }
 }
 
@@ -946,6 +971,10 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   const int64_t strips = (m + 15) / 16, nblk = k / 256;
   p.pre_bps = strips * ((nblk + 7) / 8) >= 1024 ? 8 : PRE_WAVES;
   p.pre_slices = (int)((nblk + p.pre_bps - 1) / p.pre_bps);
+  // row tiles per statistics workgroup: as many as still leave 256 workgroups
+  p.pre_tiles = 1;
+  for (int t : {4, 2})
+    if (((strips + t - 1) / t) * p.pre_slices >= 256) { p.pre_tiles = t; break; }
   p.off_amax = off;      off = align256(off + (size_t)p.pre_slices * m * 4);
   p.off_tpart = off;     off = align256(off + (size_t)p.pre_slices * m * std::max(rank, 1) * 4);
   const bool partials = p.splits > 1 || p.skinny_mt > 0;
@@ -984,19 +1013,19 @@ hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const unsigned strips = (unsigned)((p.m + 15) / 16);
-  const dim3 sgrid(strips, (unsigned)p.pre_slices);
-  if (p.rank == 0)
-    hipLaunchKernelGGL(k_fwd_stats<0>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m, p.k,
-                       p.pre_bps, b.amax, b.tpart);
-  else if (p.rank == 16)
-    hipLaunchKernelGGL(k_fwd_stats<16>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m,
-                       p.k, p.pre_bps, b.amax, b.tpart);
-  else if (p.rank == 32)
-    hipLaunchKernelGGL(k_fwd_stats<32>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m,
-                       p.k, p.pre_bps, b.amax, b.tpart);
-  else
-    hipLaunchKernelGGL(k_fwd_stats<64>, sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, p.m,
-                       p.k, p.pre_bps, b.amax, b.tpart);
+  const dim3 sgrid((unsigned)((p.m + 16 * p.pre_tiles - 1) / (16 * p.pre_tiles)), (unsigned)p.pre_slices);
+#define SQ_STATS(R, T)                                                                        \
+  hipLaunchKernelGGL((k_fwd_stats<R, T>), sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, \
+                     p.m, p.k, p.pre_bps, b.amax, b.tpart)
+#define SQ_STATS_T(R)                                                   \
+  if (p.pre_tiles == 4) SQ_STATS(R, 4); else if (p.pre_tiles == 2) SQ_STATS(R, 2); \
+  else SQ_STATS(R, 1)
+  if (p.rank == 0) { SQ_STATS_T(0); }
+  else if (p.rank == 16) { SQ_STATS_T(16); }
+  else if (p.rank == 32) { SQ_STATS_T(32); }
+  else { SQ_STATS_T(64); }
+#undef SQ_STATS_T
+#undef SQ_STATS
   if ((err = hipGetLastError()) != hipSuccess) return err;
   hipLaunchKernelGGL(k_fwd_rotate, dim3(strips, (unsigned)((p.k / 256 + PRE_WAVES - 1) / PRE_WAVES)),
                      dim3(64 * PRE_WAVES), 0, stream, x, p.m, p.k, p.rank, p.pre_slices, b.amax,
