@@ -97,13 +97,18 @@ def sets_for(set_bytes, rotate_mb):
     return max(2, int(np.ceil(rotate_mb * 1e6 / max(set_bytes, 1.0))))
 
 
+# set by --host-split: the setup's factor splits run on the host
+HOST_SPLIT = False
+
+
 def split(torch, w, rank, seed=0):
     """bf16 rank-`rank` factors (up [N, r], down [K, r]) of a device weight through
-    the builder's seeded fp64 randomized split."""
+    the builder's seeded fp64 randomized split (on the host under HOST_SPLIT)."""
     from w4_gemm_amd import builder as B
     from w4_gemm_amd.svd_init import _bf16_from_f64
-    g = torch.Generator(device=w.device).manual_seed(seed)
-    u, s, v = B.randomized_split(torch, w.double(), rank, g)
+    a = w.double().cpu() if HOST_SPLIT else w.double()
+    g = torch.Generator(device=a.device).manual_seed(seed)
+    u, s, v = B.randomized_split(torch, a, rank, g)
     rs = s[:rank].sqrt()
     up = _bf16_from_f64((u[:, :rank] * rs).cpu().numpy()).to(w.device)
     down = _bf16_from_f64((v[:, :rank] * rs).cpu().numpy()).to(w.device)
@@ -165,6 +170,9 @@ def main():
     ap.add_argument("--ops",
                     default="fwd,reconstruct,quantize,dgrad,builder,smallm,configs,w8,mx,bf16gemm")
     ap.add_argument("--small-m", default="1,16,128")
+    ap.add_argument("--host-split", action="store_true",
+                    help="run the setup's factor splits on the host (for counter passes, where "
+                         "the device QR of the split crashes the profiled process)")
     ap.add_argument("--rotate-mb", type=float, default=512.0,
                     help="least total size of the distinct sets a timed loop cycles through")
     args = ap.parse_args()
@@ -185,6 +193,8 @@ def main():
     cfg = CONFIGS[args.config]
     M, N, K, G, R = cfg.M, cfg.N, cfg.K, cfg.group, cfg.rank
     ops = args.ops.split(",")
+    global HOST_SPLIT
+    HOST_SPLIT = args.host_split
 
     # ---------------------------------------------------------------- inputs (untimed)
     t_setup = time.time()
@@ -216,6 +226,10 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    def done(section):
+        # one progress line per finished section, on stderr (the JSON line is stdout's only line)
+        print(f"[bench] {section} done at {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
     res = {}
     torch.cuda.synchronize()
     t0 = time.time()
@@ -246,11 +260,13 @@ def main():
         time.sleep(0.004)
         res["clock_under_load"] = read_clocks()
         torch.cuda.synchronize()
+        done("fwd")
     # ---------------------------------------------------------------- reconstruct
     if "reconstruct" in ops:
         res["reconstruct"] = event_times(
             torch, lambda i: W.reconstruct_bf16(payloads[i % 3], out=what[i % 3]), args.steps,
             args.warmup)
+        done("reconstruct")
     # ---------------------------------------------------------------- input gradient
     if "dgrad" in ops:
         gen = torch.Generator(device=dev).manual_seed(0)
@@ -262,30 +278,38 @@ def main():
             torch, lambda i: W.linear_dgrad(dy, dps[i % 2], out=dx, workspace=dws), args.steps,
             args.warmup)
         del dy, dx, dws
+        done("dgrad")
     # ---------------------------------------------------------------- quantize
     if "quantize" in ops:
         res["quantize"] = quantize_times(torch, W, dev, [w, w.clone()], up, down, G, args.steps,
                                          args.warmup)
+        done("quantize")
     # ---------------------------------------------------------------- int8-residual mode
     if "w8" in ops:
         res["w8"] = w8_run(torch, W, dev, w, x, what, M, N, K, args.steps, args.warmup)
+        done("w8")
     # ---------------------------------------------------------------- MXFP4 mode
     if "mx" in ops:
         res["mx"] = mx_run(torch, W, dev, w, x, up, down, what, M, N, K, args.steps, args.warmup)
+        done("mx")
     # ---------------------------------------------------------------- comparator
     if "bf16gemm" in ops:
         res["bf16gemm"] = bf16_gemm_run(torch, dev, w, x, M, N, K, args.steps, args.warmup)
+        done("bf16gemm")
     # ---------------------------------------------------------------- streaming builder
     if "builder" in ops:
         res["builder"] = builder_run(torch, dev)
+        done("builder")
     # ---------------------------------------------------------------- other shapes
     if "configs" in ops:
         res["configs"] = other_configs(torch, W, dev, [1, 2, 3, 5], max(5, args.steps // 5),
                                        args.warmup, args.rotate_mb)
+        done("configs")
     # ---------------------------------------------------------------- small-M sweep
     if "smallm" in ops and args.small_m:
         res["smallm"] = small_m_sweep(torch, W, dev, [int(v) for v in args.small_m.split(",")],
                                       args.steps, args.warmup, args.rotate_mb)
+        done("smallm")
     torch.cuda.synchronize()
     wall = time.time() - t0
 
@@ -406,6 +430,10 @@ def w8_run(torch, W, dev, w, x, what, M, N, K, steps, warmup):
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
+    def done(section):
+        # one progress line per finished section, on stderr (the JSON line is stdout's only line)
+        print(f"[bench] {section} done at {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
     def timed(fn):
         return float(np.mean(event_times(torch, fn, steps, warmup)))
 
@@ -451,6 +479,10 @@ def mx_run(torch, W, dev, w, x, up, down, what, M, N, K, steps, warmup):
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
+
+    def done(section):
+        # one progress line per finished section, on stderr (the JSON line is stdout's only line)
+        print(f"[bench] {section} done at {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
     def timed(fn):
         return float(np.mean(event_times(torch, fn, steps, warmup)))
