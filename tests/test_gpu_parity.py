@@ -216,6 +216,20 @@ def test_fwd_mid_m_plans():
         _fwd_checks(xbits, codes, scales, upb, dnb, g, rows=rows, tag=f"m{m} n{n} k{k} g{g} r{rank}")
 
 
+def test_fwd_statistics_tile_plans():
+    # long K and many rows: the statistics pass takes four and eight 16-row
+    # tiles per workgroup (at rank 64 with two x tiles in flight, at rank 32
+    # with two and four), with a ragged last row tile
+    rng = np.random.default_rng(13)
+    from synth import gen_activations
+    for (m, n, k, rank) in [(1000, 256, 16384, 64), (2040, 300, 16384, 64), (1000, 256, 16384, 32),
+                            (2040, 300, 16384, 32)]:
+        codes, scales, upb, dnb = gen_payload(rng, n, k, 32, rank)
+        xbits = gen_activations(rng, m, k, 0.01)
+        rows = np.sort(np.concatenate([rng.choice(m - 1, 15, replace=False), [m - 1]]))
+        _fwd_checks(xbits, codes, scales, upb, dnb, 32, rows=rows, tag=f"m{m} n{n} k{k} r{rank}")
+
+
 def test_fwd_decode_shapes():
     # the M <= 16 path: K slices of 512 and 1024 values, whole and with a
     # one-block last slice; N ragged against its 256-row workgroups and its

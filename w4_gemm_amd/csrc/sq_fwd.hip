@@ -68,7 +68,9 @@ __device__ __forceinline__ void load_x64(uint32_t (&xb)[32], const uint16_t* __r
 // 256-column blocks [q*bps, q*bps + bps) and the workgroup's four waves take
 // every fourth one, for TILES 16-row tiles of rows each.  A wave loads its
 // block's downT fragments (the MFMA B operand) once and contracts every row
-// tile against them, so the factor is read from L2 once per TILES tiles.
+// tile against them, so the factor is read from L2 once per TILES tiles; the
+// x loads of PF tiles are in flight at once (a ring of PF register sets), so
+// a wave streams up to PF x 8 KB of x while it contracts.
 // Writes amax_part[q][row] (bf16 magnitude bits; they order like the values)
 // and t_part[q][row][r] (fp32) for the rows below m.
 template <int RANK, int TILES>
@@ -76,6 +78,9 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ downT, int64_t m, int64_t k,
     int bps, uint32_t* __restrict__ amax_part, float* __restrict__ t_part) {
   constexpr int RT = RANK / 16;   // 16-wide rank tiles
+  // tiles in flight: the register sets that fit beside the fragments and sums
+  constexpr int PF_MAX = RANK > 32 ? 2 : TILES > 4 ? 2 : 4;
+  constexpr int PF = TILES < PF_MAX ? TILES : PF_MAX;
   __shared__ float red_t[PRE_WAVES][16][64];
   __shared__ uint32_t red_max[PRE_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -94,6 +99,15 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
     // eight of them, 32j + 8g .. +7, so the four lanes of a row read 64
     // contiguous bytes (of x and of each downT row) per instruction.
     const int64_t col = b * 256 + 8 * g;
+    u32x4 xv[PF][8];
+    auto load_tile = [&](u32x4 (&dst)[8], int tl) {
+      const int64_t lrow = min(rbase + 16 * tl + c, m - 1);   // rows past m read the last row
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        dst[j] = *reinterpret_cast<const u32x4*>(x + lrow * k + col + 32 * j);
+    };
+#pragma unroll
+    for (int tl = 0; tl < PF; ++tl) load_tile(xv[tl], tl);
     bf16x8 bfrag[RT > 0 ? RT : 1][8];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -101,19 +115,9 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
       for (int j = 0; j < 8; ++j)
         bfrag[rt][j] =
             *reinterpret_cast<const bf16x8*>(downT + (int64_t)(16 * rt + c) * k + col + 32 * j);
-    // the next tile's x is in flight while one tile is contracted
-    u32x4 xv[2][8];
-    auto load_tile = [&](u32x4 (&dst)[8], int tl) {
-      const int64_t lrow = min(rbase + 16 * tl + c, m - 1);   // rows past m read the last row
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        dst[j] = *reinterpret_cast<const u32x4*>(x + lrow * k + col + 32 * j);
-    };
-    load_tile(xv[0], 0);
 #pragma unroll
     for (int tl = 0; tl < TILES; ++tl) {
-      if (tl + 1 < TILES) load_tile(xv[(tl + 1) & 1], tl + 1);
-      const u32x4 (&xt)[8] = xv[tl & 1];
+      const u32x4 (&xt)[8] = xv[tl % PF];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -128,6 +132,8 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
         for (int rt = 0; rt < RT; ++rt)
           acc[tl][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, bfrag[rt][j], acc[tl][rt], 0, 0, 0);
       }
+      // the freed register set takes tile tl + PF
+      if (tl + PF < TILES) load_tile(xv[tl % PF], tl + PF);
     }
   }
   // per row tile: acc[tl][rt][i] = partial t[rbase + 16 tl + 4g + i][16 rt + c]
@@ -141,13 +147,15 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
       for (int i = 0; i < 4; ++i) red_t[wave][4 * g + i][16 * rt + c] = acc[tl][rt][i];
     red_max[wave][lane] = max((uint32_t)amax2[tl][0], (uint32_t)amax2[tl][1]);
     __syncthreads();
-    for (int i = tid; i < 16 * RANK; i += 64 * PRE_WAVES) {
-      const int rr = i / RANK, r = i - rr * RANK;
-      if (row0 + rr >= m) continue;
-      float t = 0.0f;
+    if constexpr (RANK > 0) {
+      for (int i = tid; i < 16 * RANK; i += 64 * PRE_WAVES) {
+        const int rr = i / RANK, r = i - rr * RANK;
+        if (row0 + rr >= m) continue;
+        float t = 0.0f;
 #pragma unroll
-      for (int w = 0; w < PRE_WAVES; ++w) t += red_t[w][rr][r];
-      t_part[(q * m + row0 + rr) * RANK + r] = t;
+        for (int w = 0; w < PRE_WAVES; ++w) t += red_t[w][rr][r];
+        t_part[(q * m + row0 + rr) * RANK + r] = t;
+      }
     }
     if (tid < 16 && row0 + tid < m) {
       uint32_t mx = 0;
@@ -966,14 +974,13 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   p.off_tlo = off;       off = align256(off + (size_t)m * std::max(rank, 1) * 2);
   p.off_rowscale = off;  off = align256(off + (size_t)m * 4);
   p.off_downT = off;     off = align256(off + (size_t)k * std::max(rank, 1) * 2);
-  // K slices of the statistics pass: two blocks per wave when that still
-  // leaves a thousand workgroups, else one
+  // K slices of the statistics pass: one 256-column block per wave
   const int64_t strips = (m + 15) / 16, nblk = k / 256;
-  p.pre_bps = strips * ((nblk + 7) / 8) >= 1024 ? 8 : PRE_WAVES;
+  p.pre_bps = PRE_WAVES;
   p.pre_slices = (int)((nblk + p.pre_bps - 1) / p.pre_bps);
   // row tiles per statistics workgroup: as many as still leave 256 workgroups
   p.pre_tiles = 1;
-  for (int t : {4, 2})
+  for (int t : {8, 4, 2})
     if (((strips + t - 1) / t) * p.pre_slices >= 256) { p.pre_tiles = t; break; }
   p.off_amax = off;      off = align256(off + (size_t)p.pre_slices * m * 4);
   p.off_tpart = off;     off = align256(off + (size_t)p.pre_slices * m * std::max(rank, 1) * 4);
@@ -1018,8 +1025,8 @@ hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t
   hipLaunchKernelGGL((k_fwd_stats<R, T>), sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, \
                      p.m, p.k, p.pre_bps, b.amax, b.tpart)
 #define SQ_STATS_T(R)                                                   \
-  if (p.pre_tiles == 4) SQ_STATS(R, 4); else if (p.pre_tiles == 2) SQ_STATS(R, 2); \
-  else SQ_STATS(R, 1)
+  if (p.pre_tiles == 8) SQ_STATS(R, 8); else if (p.pre_tiles == 4) SQ_STATS(R, 4); \
+  else if (p.pre_tiles == 2) SQ_STATS(R, 2); else SQ_STATS(R, 1)
   if (p.rank == 0) { SQ_STATS_T(0); }
   else if (p.rank == 16) { SQ_STATS_T(16); }
   else if (p.rank == 32) { SQ_STATS_T(32); }

@@ -53,7 +53,7 @@ struct FwdPlan {
   int skinny_mt;       // > 0: the small-M kernel with this many 16-row tiles
   int skinny_kslice;   // its K slice (a multiple of 256)
   int pre_bps, pre_slices;  // 256-column blocks per K slice of the statistics pass, slices
-  int pre_tiles;            // 16-row tiles per statistics workgroup (1, 2 or 4)
+  int pre_tiles;            // 16-row tiles per statistics workgroup (1, 2, 4 or 8)
   int dec;             // 1: the small-M decode path (rotation inside the contraction)
   int dec_kslice;      // its K slice (a multiple of 256, at most 1024)
   size_t off_xh, off_thi, off_tlo, off_rowscale, off_downT, off_amax, off_tpart, off_partial, total;
