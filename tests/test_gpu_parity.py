@@ -345,9 +345,12 @@ def test_dgrad_tiny(tiny):
 
 
 def test_dgrad_ragged_ranks_groups():
+    # N not a multiple of 256 (the input gradient's own statistics kernel) and
+    # N a multiple of 256 (the statistics kernel it shares with the forward)
     rng = np.random.default_rng(22)
     for (m, n, k, g, rank) in [(100, 192, 768, 64, 32), (3, 64, 256, 32, 0), (130, 128, 512, 32, 64),
-                               (257, 320, 1024, 64, 32)]:
+                               (257, 320, 1024, 64, 32), (257, 512, 1024, 32, 64),
+                               (100, 256, 768, 64, 0), (50, 768, 512, 32, 32)]:
         codes, scales, upb, dnb = gen_payload(rng, n, k, g, max(rank, 1))
         if rank == 0:
             upb = dnb = None

@@ -13,8 +13,10 @@
 // carries both terms; a single rotation of each 256-column block of C and the
 // row factor 2^(E_m-11) finish it.  Six launches on the caller's stream:
 //   1. k_dg_transpose: up [N][r] -> upT [r][N].
-//   2. k_dg_stats: per 16 rows and one slice of N, the partial row absmax of
-//      dy and the partial t = dy @ up on bf16 MFMA (one read of dy).
+//   2. the row statistics: per 16 rows and one slice of N, the partial row
+//      absmax of dy and the partial t = dy @ up on bf16 MFMA (one read of
+//      dy): the forward's statistics kernel when N is a multiple of 256,
+//      else k_dg_stats.
 //   3. k_dg_scale: E_m = ceil(log2 max|dy_m|); dy16 = fp16(dy * 2^(11-E_m))
 //      (|dy16| <= 2^11); t summed over the slices in a fixed order, times
 //      2^(11-E_m), split into bf16 hi + lo; the row factor 2^(E_m-11).
@@ -557,6 +559,10 @@ DgradPlan plan_dgrad(int64_t m, int64_t n, int64_t k, int group, int rank) {
   int64_t sps = (steps + slices - 1) / slices;
   if (sps >= 32) sps = (sps + 31) / 32 * 32;   // whole units for all four waves
   p.stats_sps = (int)sps;
+  // N a multiple of 256: the shared row-statistics kernel (one 256-column
+  // block of N per wave, several 16-row tiles against one read of its upT
+  // fragments)
+  p.stats_tiles = 0;
   // contraction tile height: the one with the fewest rows x rounds of 256 CUs
   {
     const int64_t kt = k / 256;
@@ -564,6 +570,7 @@ DgradPlan plan_dgrad(int64_t m, int64_t n, int64_t k, int group, int rank) {
     p.tile_m = cost(224) < cost(256) ? 224 : 256;
   }
   p.stats_slices = (int)((steps + sps - 1) / sps);
+  if (n % 256 == 0) row_stats_plan(m, n, &p.stats_tiles, &p.stats_slices);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -597,16 +604,22 @@ hipError_t launch_dgrad(const DgradPlan& p, const uint16_t* dy, const uint8_t* c
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const dim3 sgrid(strips, (unsigned)p.stats_slices);
-  if (p.rank == 0)
-    hipLaunchKernelGGL(k_dg_stats<0>, sgrid, dim3(64 * DG_WAVES), 0, stream, dy, b.upT, p.m, p.n,
-                       p.stats_sps, b.amax, b.tpart);
-  else if (p.rank == 32)
-    hipLaunchKernelGGL(k_dg_stats<32>, sgrid, dim3(64 * DG_WAVES), 0, stream, dy, b.upT, p.m,
-                       p.n, p.stats_sps, b.amax, b.tpart);
-  else
-    hipLaunchKernelGGL(k_dg_stats<64>, sgrid, dim3(64 * DG_WAVES), 0, stream, dy, b.upT, p.m,
-                       p.n, p.stats_sps, b.amax, b.tpart);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (p.stats_tiles > 0) {
+    if ((err = launch_row_stats(dy, b.upT, p.m, p.n, p.rank, p.stats_tiles, p.stats_slices,
+                                b.amax, b.tpart, stream)) != hipSuccess)
+      return err;
+  } else {
+    if (p.rank == 0)
+      hipLaunchKernelGGL(k_dg_stats<0>, sgrid, dim3(64 * DG_WAVES), 0, stream, dy, b.upT, p.m,
+                         p.n, p.stats_sps, b.amax, b.tpart);
+    else if (p.rank == 32)
+      hipLaunchKernelGGL(k_dg_stats<32>, sgrid, dim3(64 * DG_WAVES), 0, stream, dy, b.upT, p.m,
+                         p.n, p.stats_sps, b.amax, b.tpart);
+    else
+      hipLaunchKernelGGL(k_dg_stats<64>, sgrid, dim3(64 * DG_WAVES), 0, stream, dy, b.upT, p.m,
+                         p.n, p.stats_sps, b.amax, b.tpart);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(k_dg_scale, dim3(strips, (unsigned)((p.n + 255) / 256)), dim3(256), 0, stream,
                      dy, p.m, p.n, p.rank, p.stats_slices, b.amax, b.tpart, b.dy16, b.thi, b.tlo,
                      b.rowscale);

@@ -974,14 +974,9 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   p.off_tlo = off;       off = align256(off + (size_t)m * std::max(rank, 1) * 2);
   p.off_rowscale = off;  off = align256(off + (size_t)m * 4);
   p.off_downT = off;     off = align256(off + (size_t)k * std::max(rank, 1) * 2);
-  // K slices of the statistics pass: one 256-column block per wave
-  const int64_t strips = (m + 15) / 16, nblk = k / 256;
+  // statistics pass: one 256-column block per wave, K slices of four blocks
   p.pre_bps = PRE_WAVES;
-  p.pre_slices = (int)((nblk + p.pre_bps - 1) / p.pre_bps);
-  // row tiles per statistics workgroup: as many as still leave 256 workgroups
-  p.pre_tiles = 1;
-  for (int t : {8, 4, 2})
-    if (((strips + t - 1) / t) * p.pre_slices >= 256) { p.pre_tiles = t; break; }
+  row_stats_plan(m, k, &p.pre_tiles, &p.pre_slices);
   p.off_amax = off;      off = align256(off + (size_t)p.pre_slices * m * 4);
   p.off_tpart = off;     off = align256(off + (size_t)p.pre_slices * m * std::max(rank, 1) * 4);
   const bool partials = p.splits > 1 || p.skinny_mt > 0;
@@ -1009,6 +1004,34 @@ static FwdBuffers carve(const FwdPlan& p, void* workspace) {
                     reinterpret_cast<float*>(ws + p.off_tpart)};
 }
 
+// Row tiles per statistics workgroup: as many as still leave 256 workgroups.
+void row_stats_plan(int64_t m, int64_t k, int* tiles, int* slices) {
+  const int64_t strips = (m + 15) / 16, nblk = k / 256;
+  *slices = (int)((nblk + PRE_WAVES - 1) / PRE_WAVES);
+  *tiles = 1;
+  for (int t : {8, 4, 2})
+    if (((strips + t - 1) / t) * *slices >= 256) { *tiles = t; break; }
+}
+
+hipError_t launch_row_stats(const uint16_t* a, const uint16_t* bT, int64_t m, int64_t k, int rank,
+                            int tiles, int slices, uint32_t* amax_part, float* t_part,
+                            hipStream_t stream) {
+  const dim3 sgrid((unsigned)((m + 16 * tiles - 1) / (16 * tiles)), (unsigned)slices);
+#define SQ_STATS(R, T)                                                                     \
+  hipLaunchKernelGGL((k_fwd_stats<R, T>), sgrid, dim3(64 * PRE_WAVES), 0, stream, a, bT, m, k, \
+                     PRE_WAVES, amax_part, t_part)
+#define SQ_STATS_T(R)                                                                    \
+  if (tiles == 8) SQ_STATS(R, 8); else if (tiles == 4) SQ_STATS(R, 4);                   \
+  else if (tiles == 2) SQ_STATS(R, 2); else SQ_STATS(R, 1)
+  if (rank == 0) { SQ_STATS_T(0); }
+  else if (rank == 16) { SQ_STATS_T(16); }
+  else if (rank == 32) { SQ_STATS_T(32); }
+  else { SQ_STATS_T(64); }
+#undef SQ_STATS_T
+#undef SQ_STATS
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t* down,
                              void* workspace, hipStream_t stream) {
   const FwdBuffers b = carve(p, workspace);
@@ -1020,20 +1043,9 @@ hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const unsigned strips = (unsigned)((p.m + 15) / 16);
-  const dim3 sgrid((unsigned)((p.m + 16 * p.pre_tiles - 1) / (16 * p.pre_tiles)), (unsigned)p.pre_slices);
-#define SQ_STATS(R, T)                                                                        \
-  hipLaunchKernelGGL((k_fwd_stats<R, T>), sgrid, dim3(64 * PRE_WAVES), 0, stream, x, b.downT, \
-                     p.m, p.k, p.pre_bps, b.amax, b.tpart)
-#define SQ_STATS_T(R)                                                   \
-  if (p.pre_tiles == 8) SQ_STATS(R, 8); else if (p.pre_tiles == 4) SQ_STATS(R, 4); \
-  else if (p.pre_tiles == 2) SQ_STATS(R, 2); else SQ_STATS(R, 1)
-  if (p.rank == 0) { SQ_STATS_T(0); }
-  else if (p.rank == 16) { SQ_STATS_T(16); }
-  else if (p.rank == 32) { SQ_STATS_T(32); }
-  else { SQ_STATS_T(64); }
-#undef SQ_STATS_T
-#undef SQ_STATS
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_row_stats(x, b.downT, p.m, p.k, p.rank, p.pre_tiles, p.pre_slices, b.amax,
+                              b.tpart, stream)) != hipSuccess)
+    return err;
   hipLaunchKernelGGL(k_fwd_rotate, dim3(strips, (unsigned)((p.k / 256 + PRE_WAVES - 1) / PRE_WAVES)),
                      dim3(64 * PRE_WAVES), 0, stream, x, p.m, p.k, p.rank, p.pre_slices, b.amax,
                      b.tpart, b.xh, b.thi, b.tlo, b.rowscale);
