@@ -130,6 +130,41 @@ __device__ __forceinline__ void xcd_tile(int64_t lin, int64_t tiles, int64_t nt,
 
 // Slot of 16-byte chunk c in row r is c ^ a_swz(r): the 16 rows read by one
 // fragment load land in distinct bank groups whether the LDS has 32 or 64 banks.
+// Maximum over `slices` partial row maxima part[q * stride] (q in order), with
+// eight loads in flight at a time: a loop of single loads would wait out one
+// memory round trip per slice.
+__device__ __forceinline__ uint32_t slice_max(const uint32_t* __restrict__ part, int64_t stride,
+                                              int slices) {
+  uint32_t mx = 0;
+  int q = 0;
+  for (; q + 8 <= slices; q += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(q + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mx = max(mx, v[u]);
+  }
+  for (; q < slices; ++q) mx = max(mx, part[q * stride]);
+  return mx;
+}
+
+// Sum in slice order of `slices` fp32 partials part[q * stride], eight loads
+// in flight at a time.
+__device__ __forceinline__ float slice_sum(const float* __restrict__ part, int64_t stride,
+                                           int slices) {
+  float t = 0.0f;
+  int q = 0;
+  for (; q + 8 <= slices; q += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(q + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t += v[u];
+  }
+  for (; q < slices; ++q) t += part[q * stride];
+  return t;
+}
+
 __device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // ---------------------------------------------------------------------------

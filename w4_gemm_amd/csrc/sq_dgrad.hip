@@ -139,9 +139,7 @@ __global__ void __launch_bounds__(256) k_dg_scale(
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   if (tid < 16) {
     const int64_t row = min(row0 + tid, m - 1);
-    uint32_t mx = 0;
-    for (int q = 0; q < slices; ++q) mx = max(mx, amax_part[q * m + row]);
-    s_exp[tid] = row_exponent(mx);
+    s_exp[tid] = row_exponent(slice_max(amax_part + row, m, slices));
   }
   __syncthreads();
   {
@@ -154,8 +152,7 @@ __global__ void __launch_bounds__(256) k_dg_scale(
       const int rr = i / rank, r = i - rr * rank;
       const int64_t row = row0 + rr;
       if (row >= m) continue;
-      float t = 0.0f;
-      for (int q = 0; q < slices; ++q) t += t_part[(q * m + row) * rank + r];
+      float t = slice_sum(t_part + row * rank + r, m * rank, slices);
       t *= ldexpf(1.0f, 11 - s_exp[rr]);
       const uint16_t hb = f32_to_bf16(t);
       thi[row * rank + r] = hb;

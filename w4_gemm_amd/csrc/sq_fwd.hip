@@ -185,9 +185,7 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
   // E of the workgroup's rows (rows past m repeat the last row)
   if (tid < 16) {
     const int64_t row = min(row0 + tid, m - 1);
-    uint32_t mx = 0;
-    for (int q = 0; q < slices; ++q) mx = max(mx, amax_part[q * m + row]);
-    s_exp[tid] = row_exponent(mx);
+    s_exp[tid] = row_exponent(slice_max(amax_part + row, m, slices));
   }
   __syncthreads();
 
@@ -202,16 +200,7 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
       const int rr = i / rank, r = i - rr * rank;
       const int64_t row = row0 + rr;
       if (row >= m) continue;
-      float t = 0.0f;
-      int q = 0;
-      for (; q + 8 <= slices; q += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = t_part[((q + u) * m + row) * rank + r];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) t += v[u];
-      }
-      for (; q < slices; ++q) t += t_part[(q * m + row) * rank + r];
+      float t = slice_sum(t_part + row * rank + r, m * rank, slices);
       t *= ldexpf(1.0f, 11 - s_exp[rr]);
       const uint16_t hb = f32_to_bf16(t);
       thi[row * rank + r] = hb;
