@@ -11,9 +11,11 @@ on (torch's current stream), after warm-up calls.  Every timed loop cycles
 through distinct input/output sets of at least 512 MB in total (two whole
 forward sets of payload, x, y and workspace; enough payload copies for the
 small-M graphs; three reconstruct sets; two quantizer inputs), so the 256 MB
-Infinity Cache cannot serve the next call from the previous one.  The headline `value` is the fused forward's TFLOP/s at
-4480x16384x6144 (flops = 2MNK + 2Mr(N+K)); reconstruct GB/s and quantize
-GB/s are reported beside it.
+Infinity Cache cannot serve the next call from the previous one, and runs the
+same launches back to back for 0.2 s first (after an idle gap the clock ramps
+up over the first milliseconds of load).  The headline `value` is the fused
+forward's TFLOP/s at 4480x16384x6144 (flops = 2MNK + 2Mr(N+K)); reconstruct
+GB/s and quantize GB/s are reported beside it.
 
 The `roofline` object is for the forward's dominant kernel (the contraction,
 k_fwd_gemm_big, timed alone through sq_linear_fwd_contract).  Its `traffic`
@@ -22,7 +24,7 @@ is the HBM bytes per launch that rocprofv3 counters measured for that kernel
 bytes of a plain device copy), read from the committed counter summary under
 profiles/; it is null when the kernel source has changed since then.
 `cpu_baseline` is the CPU oracle's forward on a sample of rows, on this
-host's cores.
+host's cores, with the BLAS library and the thread and CPU counts.
 
 Extra fields: the input gradient (sq_linear_dgrad, dx = dy W_hat, same
 flop count as the forward, not part of the step), the streaming builder's
@@ -42,6 +44,9 @@ clock levels.
 
 Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--config 4]
        python bench.py --ops copy      (the counter calibration copy only)
+       python bench.py --ops fwd --host-split   (for counter passes: the setup's
+                                                 factor split runs on the host)
+One JSON line goes to stdout; one progress line per finished section to stderr.
 """
 from __future__ import annotations
 
