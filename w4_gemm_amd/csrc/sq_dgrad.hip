@@ -594,7 +594,10 @@ hipError_t launch_dgrad(const DgradPlan& p, const uint16_t* dy, const uint8_t* c
   const DgBuffers b = carve(p, workspace);
   hipError_t err;
   const unsigned strips = (unsigned)((p.m + 15) / 16);
-  if (p.rank > 0) {
+  // the shared statistics kernel reads lora_up as stored at ranks 16 and 32;
+  // rank 64 and the kernel for N not a multiple of 256 read a transposed copy
+  const bool kmajor = p.stats_tiles > 0 && p.rank > 0 && p.rank <= 32;
+  if (p.rank > 0 && !kmajor) {
     const int64_t cnt = p.n * p.rank;
     hipLaunchKernelGGL(k_dg_transpose, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
                        up, b.upT, p.n, p.rank);
@@ -602,8 +605,8 @@ hipError_t launch_dgrad(const DgradPlan& p, const uint16_t* dy, const uint8_t* c
   }
   const dim3 sgrid(strips, (unsigned)p.stats_slices);
   if (p.stats_tiles > 0) {
-    if ((err = launch_row_stats(dy, b.upT, p.m, p.n, p.rank, p.stats_tiles, p.stats_slices,
-                                b.amax, b.tpart, stream)) != hipSuccess)
+    if ((err = launch_row_stats(dy, kmajor ? up : b.upT, kmajor, p.m, p.n, p.rank, p.stats_tiles,
+                                p.stats_slices, b.amax, b.tpart, stream)) != hipSuccess)
       return err;
   } else {
     if (p.rank == 0)

@@ -67,21 +67,30 @@ __device__ __forceinline__ void load_x64(uint32_t (&xb)[32], const uint16_t* __r
 // Pass 1: grid (ceil(m / (16 TILES)), slices); slice q covers the
 // 256-column blocks [q*bps, q*bps + bps) and the workgroup's four waves take
 // every fourth one, for TILES 16-row tiles of rows each.  A wave loads its
-// block's downT fragments (the MFMA B operand) once and contracts every row
-// tile against them, so the factor is read from L2 once per TILES tiles; the
-// x loads of PF tiles are in flight at once (a ring of PF register sets), so
-// a wave streams up to PF x 8 KB of x while it contracts.
+// block's factor fragments (the MFMA B operand) once and contracts every row
+// tile against them, so the factor is read once per TILES tiles; the x loads
+// of PF tiles are in flight at once (a ring of PF register sets), so a wave
+// streams up to PF x 8 KB of x while it contracts.
+// KMAJOR: the factor is given as stored, [k][RANK] (lora_down, or lora_up
+// for the input gradient): each wave stages its block's 256 rows of it in
+// LDS with direct loads, issued ahead of its x loads, and gathers its
+// fragments there (the area then holds the wave's reduction scratch).  Else
+// it is given transposed, [RANK][k], and the fragments are read from it.
 // Writes amax_part[q][row] (bf16 magnitude bits; they order like the values)
 // and t_part[q][row][r] (fp32) for the rows below m.
-template <int RANK, int TILES>
+template <int RANK, int TILES, bool KMAJOR>
 __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ downT, int64_t m, int64_t k,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ fac, int64_t m, int64_t k,
     int bps, uint32_t* __restrict__ amax_part, float* __restrict__ t_part) {
+  static_assert(!KMAJOR || (RANK > 0 && RANK <= 32), "staged factor: ranks 16 and 32");
   constexpr int RT = RANK / 16;   // 16-wide rank tiles
   // tiles in flight: the register sets that fit beside the fragments and sums
   constexpr int PF_MAX = RANK > 32 ? 2 : TILES > 4 ? 2 : 4;
   constexpr int PF = TILES < PF_MAX ? TILES : PF_MAX;
-  __shared__ float red_t[PRE_WAVES][16][64];
+  // per wave: its block's factor rows (KMAJOR), or at least its 16 x 64 fp32 sums
+  constexpr int WAVE_LDS = KMAJOR ? 256 * RANK * 2 : 16 * 64 * 4;
+  static_assert(WAVE_LDS >= 16 * 64 * 4, "the sums fit the staging area");
+  __shared__ __attribute__((aligned(16))) uint8_t wave_lds[PRE_WAVES][WAVE_LDS];
   __shared__ uint32_t red_max[PRE_WAVES][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -97,8 +106,21 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
   for (int64_t b = q * bps + wave; b < b_end; b += PRE_WAVES) {
     // MFMA j contracts columns 32j .. 32j+31 of the block; lane (c, g) holds
     // eight of them, 32j + 8g .. +7, so the four lanes of a row read 64
-    // contiguous bytes (of x and of each downT row) per instruction.
+    // contiguous bytes (of x and of each factor row) per instruction.
     const int64_t col = b * 256 + 8 * g;
+    constexpr int NSTAGE = KMAJOR ? 256 * RANK * 2 / 1024 : 0;   // 1 KB direct loads
+    if constexpr (KMAJOR) {
+      // the block's 256 factor rows (256 * RANK * 2 contiguous bytes) go to
+      // this wave's LDS area first; the x loads below are issued behind them
+      const __amdgpu_buffer_rsrc_t f_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(fac + b * 256 * RANK), (short)0, 256 * RANK * 2, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < NSTAGE; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            f_rsrc, (__attribute__((address_space(3))) void*)(&wave_lds[wave][0] + i * 1024), 16,
+            (uint32_t)(lane * 16 + i * 1024), 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     u32x4 xv[PF][8];
     auto load_tile = [&](u32x4 (&dst)[8], int tl) {
       const int64_t lrow = min(rbase + 16 * tl + c, m - 1);   // rows past m read the last row
@@ -109,12 +131,33 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
 #pragma unroll
     for (int tl = 0; tl < PF; ++tl) load_tile(xv[tl], tl);
     bf16x8 bfrag[RT > 0 ? RT : 1][8];
+    if constexpr (KMAJOR) {
+      // the staged rows have landed once no more than the x loads behind
+      // them are outstanding (loads complete in order)
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int XL = PF * 8;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (XL & 15) | ((XL >> 4) << 14));
+      __builtin_amdgcn_sched_barrier(0);
+      // element e of fragment (rt, j): factor row 32j + 8g + e, column 16rt + c
+      const uint16_t* st = reinterpret_cast<const uint16_t*>(&wave_lds[wave][0]);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        bfrag[rt][j] =
-            *reinterpret_cast<const bf16x8*>(downT + (int64_t)(16 * rt + c) * k + col + 32 * j);
+        for (int j = 0; j < 8; ++j) {
+          bf16x8 f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            f[e] = __builtin_bit_cast(__bf16, st[(32 * j + 8 * g + e) * RANK + 16 * rt + c]);
+          bfrag[rt][j] = f;
+        }
+    } else {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          bfrag[rt][j] =
+              *reinterpret_cast<const bf16x8*>(fac + (int64_t)(16 * rt + c) * k + col + 32 * j);
+    }
 #pragma unroll
     for (int tl = 0; tl < TILES; ++tl) {
       const u32x4 (&xt)[8] = xv[tl % PF];
@@ -124,7 +167,7 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
         for (int e = 0; e < 4; ++e)
           amax2[tl] =
               __builtin_elementwise_max(amax2[tl], __builtin_bit_cast(u16x2, xt[j][e] & 0x7FFF7FFFu));
-      // t: A = x (row c), B = downT (r = 16rt + c), both over the same columns
+      // t: A = x (row c), B = the factor (r = 16rt + c), both over the same columns
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const bf16x8 afrag = __builtin_bit_cast(bf16x8, xt[j]);
@@ -136,7 +179,10 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
       if (tl + PF < TILES) load_tile(xv[tl % PF], tl + PF);
     }
   }
-  // per row tile: acc[tl][rt][i] = partial t[rbase + 16 tl + 4g + i][16 rt + c]
+  // per row tile: acc[tl][rt][i] = partial t[rbase + 16 tl + 4g + i][16 rt + c];
+  // wave w's sums go to the start of its own LDS area (after its factor
+  // fragments have been read from there)
+  auto red_t = [&](int w) { return reinterpret_cast<float(*)[64]>(&wave_lds[w][0]); };
 #pragma unroll
   for (int tl = 0; tl < TILES; ++tl) {
     const int64_t row0 = rbase + 16 * tl;
@@ -144,7 +190,7 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red_t[wave][4 * g + i][16 * rt + c] = acc[tl][rt][i];
+      for (int i = 0; i < 4; ++i) red_t(wave)[4 * g + i][16 * rt + c] = acc[tl][rt][i];
     red_max[wave][lane] = max((uint32_t)amax2[tl][0], (uint32_t)amax2[tl][1]);
     __syncthreads();
     if constexpr (RANK > 0) {
@@ -153,7 +199,7 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
         if (row0 + rr >= m) continue;
         float t = 0.0f;
 #pragma unroll
-        for (int w = 0; w < PRE_WAVES; ++w) t += red_t[w][rr][r];
+        for (int w = 0; w < PRE_WAVES; ++w) t += red_t(w)[rr][r];
         t_part[(q * m + row0 + rr) * RANK + r] = t;
       }
     }
@@ -1002,20 +1048,20 @@ void row_stats_plan(int64_t m, int64_t k, int* tiles, int* slices) {
     if (((strips + t - 1) / t) * *slices >= 256) { *tiles = t; break; }
 }
 
-hipError_t launch_row_stats(const uint16_t* a, const uint16_t* bT, int64_t m, int64_t k, int rank,
-                            int tiles, int slices, uint32_t* amax_part, float* t_part,
-                            hipStream_t stream) {
+hipError_t launch_row_stats(const uint16_t* a, const uint16_t* fac, bool kmajor, int64_t m,
+                            int64_t k, int rank, int tiles, int slices, uint32_t* amax_part,
+                            float* t_part, hipStream_t stream) {
   const dim3 sgrid((unsigned)((m + 16 * tiles - 1) / (16 * tiles)), (unsigned)slices);
-#define SQ_STATS(R, T)                                                                     \
-  hipLaunchKernelGGL((k_fwd_stats<R, T>), sgrid, dim3(64 * PRE_WAVES), 0, stream, a, bT, m, k, \
-                     PRE_WAVES, amax_part, t_part)
-#define SQ_STATS_T(R)                                                                    \
-  if (tiles == 8) SQ_STATS(R, 8); else if (tiles == 4) SQ_STATS(R, 4);                   \
-  else if (tiles == 2) SQ_STATS(R, 2); else SQ_STATS(R, 1)
-  if (rank == 0) { SQ_STATS_T(0); }
-  else if (rank == 16) { SQ_STATS_T(16); }
-  else if (rank == 32) { SQ_STATS_T(32); }
-  else { SQ_STATS_T(64); }
+#define SQ_STATS(R, T, KM)                                                                      \
+  hipLaunchKernelGGL((k_fwd_stats<R, T, KM>), sgrid, dim3(64 * PRE_WAVES), 0, stream, a, fac, m, \
+                     k, PRE_WAVES, amax_part, t_part)
+#define SQ_STATS_T(R, KM)                                                                 \
+  if (tiles == 8) SQ_STATS(R, 8, KM); else if (tiles == 4) SQ_STATS(R, 4, KM);            \
+  else if (tiles == 2) SQ_STATS(R, 2, KM); else SQ_STATS(R, 1, KM)
+  if (rank == 0) { SQ_STATS_T(0, false); }
+  else if (rank == 16) { if (kmajor) { SQ_STATS_T(16, true); } else { SQ_STATS_T(16, false); } }
+  else if (rank == 32) { if (kmajor) { SQ_STATS_T(32, true); } else { SQ_STATS_T(32, false); } }
+  else { SQ_STATS_T(64, false); }
 #undef SQ_STATS_T
 #undef SQ_STATS
   return hipGetLastError();
@@ -1025,15 +1071,18 @@ hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t
                              void* workspace, hipStream_t stream) {
   const FwdBuffers b = carve(p, workspace);
   hipError_t err;
-  if (p.rank > 0) {
+  // ranks 16 and 32: the statistics pass reads lora_down as stored; rank 64
+  // (whose staged rows would not fit beside the sums) reads a transposed copy
+  const bool kmajor = p.rank > 0 && p.rank <= 32;
+  if (p.rank > 0 && !kmajor) {
     const int64_t cnt = p.k * p.rank;
     hipLaunchKernelGGL(k_transpose_down, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, stream,
                        down, b.downT, p.k, p.rank);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const unsigned strips = (unsigned)((p.m + 15) / 16);
-  if ((err = launch_row_stats(x, b.downT, p.m, p.k, p.rank, p.pre_tiles, p.pre_slices, b.amax,
-                              b.tpart, stream)) != hipSuccess)
+  if ((err = launch_row_stats(x, kmajor ? down : b.downT, kmajor, p.m, p.k, p.rank, p.pre_tiles,
+                              p.pre_slices, b.amax, b.tpart, stream)) != hipSuccess)
     return err;
   hipLaunchKernelGGL(k_fwd_rotate, dim3(strips, (unsigned)((p.k / 256 + PRE_WAVES - 1) / PRE_WAVES)),
                      dim3(64 * PRE_WAVES), 0, stream, x, p.m, p.k, p.rank, p.pre_slices, b.amax,

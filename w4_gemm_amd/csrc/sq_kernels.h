@@ -73,15 +73,17 @@ hipError_t launch_decode_contract(const FwdPlan& plan, const uint16_t* x, const 
                                   void* y, int y_bf16, void* workspace, hipStream_t stream);
 
 // Row statistics of a bf16 matrix a [m][k] (k a multiple of 256) against a
-// bf16 factor bT [rank][k]: per K slice of four 256-column blocks, the row
-// absmax bits amax_part[q][row] and the partial products
-// t_part[q][row][r] = sum_{k in slice q} a[row][k] bT[r][k] (fp32, fixed
-// order).  rank is 0, 16, 32 or 64; tiles (1, 2, 4 or 8) 16-row tiles per
-// workgroup.  row_stats_plan picks the tiles and the slice count.
+// bf16 factor: per K slice of four 256-column blocks, the row absmax bits
+// amax_part[q][row] and the partial products
+// t_part[q][row][r] = sum_{k in slice q} a[row][k] fac[k][r] (fp32, fixed
+// order).  The factor is [k][rank] when kmajor (ranks 16 and 32 only), else
+// transposed, [rank][k].  rank is 0, 16, 32 or 64; tiles (1, 2, 4 or 8)
+// 16-row tiles per workgroup.  row_stats_plan picks the tiles and the slice
+// count.
 void row_stats_plan(int64_t m, int64_t k, int* tiles, int* slices);
-hipError_t launch_row_stats(const uint16_t* a, const uint16_t* bT, int64_t m, int64_t k, int rank,
-                            int tiles, int slices, uint32_t* amax_part, float* t_part,
-                            hipStream_t stream);
+hipError_t launch_row_stats(const uint16_t* a, const uint16_t* fac, bool kmajor, int64_t m,
+                            int64_t k, int rank, int tiles, int slices, uint32_t* amax_part,
+                            float* t_part, hipStream_t stream);
 hipError_t launch_fwd_rotate(const FwdPlan& plan, const uint16_t* x, const uint16_t* down,
                              void* workspace, hipStream_t stream);
 hipError_t launch_fwd_contract(const FwdPlan& plan, const uint8_t* codes, const uint16_t* scales,
