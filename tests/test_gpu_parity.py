@@ -230,6 +230,34 @@ def test_fwd_statistics_tile_plans():
         _fwd_checks(xbits, codes, scales, upb, dnb, 32, rows=rows, tag=f"m{m} n{n} k{k} r{rank}")
 
 
+def test_fwd_one_launch_prephase():
+    # K <= 4096 at ranks 0 and 32 with M > 16: the statistics and rotation run
+    # in one launch, a workgroup per 16-row strip whose eight waves take one or
+    # two 256-column blocks each: one block in all (K = 256), nine (the first
+    # wave two, the other seven one), sixteen (two each); M ragged against the
+    # strips; the split rotate + contract calls give the one-call result bit
+    # for bit
+    import w4_gemm_amd as W
+    rng = np.random.default_rng(14)
+    from synth import gen_activations
+    for (m, n, k, g, rank) in [(40, 96, 256, 32, 32), (33, 300, 2304, 64, 0),
+                               (77, 128, 4096, 32, 32), (300, 260, 2304, 32, 32)]:
+        codes, scales, upb, dnb = gen_payload(rng, n, k, g, max(rank, 1))
+        if rank == 0:
+            upb = dnb = None
+        xbits = gen_activations(rng, m, k, 0.01)
+        _fwd_checks(xbits, codes, scales, upb, dnb, g, tag=f"m{m} n{n} k{k} g{g} r{rank}")
+        p = to_dev_payload(codes, scales, upb, dnb, g)
+        xd = _x_dev(xbits)
+        ws = torch.empty(W.fwd_workspace_bytes(m, p), dtype=torch.uint8, device=dev())
+        y1 = W.linear_fwd(xd, p, torch.float32, workspace=ws)
+        y2 = torch.empty_like(y1)
+        W.linear_fwd_rotate(xd, p, ws)
+        W.linear_fwd_contract(m, p, y2, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+
+
 def test_fwd_decode_shapes():
     # the M <= 16 path: K slices of 512 and 1024 values, whole and with a
     # one-block last slice; N ragged against its 256-row workgroups and its

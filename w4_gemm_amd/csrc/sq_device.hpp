@@ -33,6 +33,10 @@ constexpr int SQ_CPOL_NT = 2;
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0]+[15:14], expcnt [6:4],
 // lgkmcnt [11:8]): wait for all vector memory operations, others untouched.
 constexpr int SQ_WAIT_VM0 = 0x0F70;
+// wait until at most n vector memory operations are outstanding (n < 64)
+constexpr int sq_wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+// wait for all LDS (and scalar memory) operations, the rest untouched
+constexpr int SQ_WAIT_LGKM0 = 0xC07F;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

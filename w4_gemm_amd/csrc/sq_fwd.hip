@@ -5,18 +5,19 @@
 //   y[m][n] = 2^(E_m - 11) * ( sum_k xh16[m][k] * fp16(q[n][k] s[n][k/G])
 //                              + sum_r t16[m][r] * up[n][r] )
 //
-// Four launches on the caller's stream:
-//   1. k_transpose_down: down [K][r] -> downT [r][K] (tiny; lets the MFMA
-//      operands of x @ down be read as 16-byte rows).
-//   2. k_fwd_stats: per 16 rows and one slice of K, the partial row absmax
-//      and the partial t = x @ down on bf16 MFMA (one read of x).
-//   3. k_fwd_rotate: per 16 rows x one 256-column block, E_m = ceil(log2 A_m)
+// Launches on the caller's stream:
+//   1. k_fwd_stats: per 16 rows and one slice of K, the partial row absmax
+//      and the partial t = x @ down on bf16 MFMA (one read of x).  At rank 64
+//      a tiny k_transpose_down (down [K][r] -> downT [r][K]) runs first.
+//   2. k_fwd_rotate: per 16 rows x one 256-column block, E_m = ceil(log2 A_m)
 //      from the slices' maxima and xh = (x H) * 2^(11-E_m) with the 256-point
 //      butterflies in registers and lane swaps, rounded to fp16 (|xh| <= 2^15
 //      because every entry of x H is at most 16 A_m) and stored through an
 //      LDS transpose; the first column group also adds the slices of t in a
 //      fixed order and splits t * 2^(11-E_m) into bf16 hi + lo.
-//   4. k_fwd_gemm: the int4 contraction on fp16 MFMA.  The packed codes stream
+//      For K <= 4096 at ranks 0, 16 and 32, k_fwd_prep does 1 and 2 in one
+//      launch, one workgroup per 16-row strip.
+//   3. k_fwd_gemm_big (M > 64) or k_fwd_skinny: the int4 contraction on fp16 MFMA.  The packed codes stream
 //      from HBM as 16-byte loads, become fp16(q*s) in LDS (one rounding of the
 //      exact product), and meet the fp16 activations; the rank-r branch is two
 //      bf16 MFMA passes (hi and lo) into the same accumulators; the epilogue
@@ -136,7 +137,7 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
       // them are outstanding (loads complete in order)
       __builtin_amdgcn_sched_barrier(0);
       constexpr int XL = PF * 8;
-      __builtin_amdgcn_s_waitcnt(0x0F70 | (XL & 15) | ((XL >> 4) << 14));
+      __builtin_amdgcn_s_waitcnt(sq_wait_vm(XL));
       __builtin_amdgcn_sched_barrier(0);
       // element e of fragment (rt, j): factor row 32j + 8g + e, column 16rt + c
       const uint16_t* st = reinterpret_cast<const uint16_t*>(&wave_lds[wave][0]);
@@ -297,6 +298,189 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
   for (int j = 0; j < 8; ++j) {
     const u32x4 o = stage[(2 * j + (lane >> 5)) * PRE_STAGE_U4 + (lane & 31)];
     __builtin_amdgcn_raw_buffer_store_b128(o, rsrc, off + (uint32_t)(4 * j) * (uint32_t)k, 0, 0);
+  }
+}
+
+// Both passes in one launch, for K <= 256 * PREP_WAVES * NB and ranks 0, 16
+// and 32: workgroup i owns rows 16i .. 16i+15 over all of K, and wave w the
+// 256-column blocks w, w + PREP_WAVES, ... (at most NB of them), whose x it
+// loads once, in the rotation's lane layout (lane (c, g): row c, columns
+// 64g .. 64g+63), and keeps in registers.  The t MFMAs take their K slots in
+// that layout too: slot (g, e) of MFMA j is column 64g + 8j + e of the block,
+// for x (A) and for the staged lora_down rows (B) alike, so the sum is the
+// same dot product over the block.  The row maxima and the waves' t sums meet
+// in LDS; then every wave rotates its blocks from registers and stores them
+// as the rotation pass does.  At these sizes the two passes are two short
+// launches, each mostly latency.
+constexpr int PREP_WAVES = 8;
+constexpr int PREP_MAX_NB = 2;
+
+template <int RANK, int NB>
+__global__ void __launch_bounds__(64 * PREP_WAVES) k_fwd_prep(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ down, int64_t m, int64_t k,
+    uint16_t* __restrict__ xh, uint16_t* __restrict__ thi, uint16_t* __restrict__ tlo,
+    float* __restrict__ rowscale) {
+  static_assert(RANK == 0 || RANK == 16 || RANK == 32, "staged factor: ranks 16 and 32");
+  static_assert(NB >= 1 && NB <= PREP_MAX_NB, "blocks per wave");
+  constexpr int RT = RANK / 16;
+  constexpr int STAGE_BYTES = 16 * PRE_STAGE_U4 * 16;   // the store staging of one block
+  constexpr int FAC_BYTES = 256 * RANK * 2;              // one block's lora_down rows
+  constexpr int SUM_BYTES = 16 * (RANK > 0 ? RANK : 1) * 4;
+  constexpr int WAVE_LDS = STAGE_BYTES > FAC_BYTES ? (STAGE_BYTES > SUM_BYTES ? STAGE_BYTES : SUM_BYTES)
+                                                   : (FAC_BYTES > SUM_BYTES ? FAC_BYTES : SUM_BYTES);
+  __shared__ __attribute__((aligned(16))) uint8_t wave_lds[PREP_WAVES][WAVE_LDS];
+  __shared__ uint32_t red_max[PREP_WAVES][64];
+  __shared__ int s_exp[16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t lrow = min(row0 + c, m - 1);   // rows past m read the last row
+  const int nblk = (int)(k >> 8);
+  const int nown = wave < nblk ? min(NB, (nblk - wave + PREP_WAVES - 1) / PREP_WAVES) : 0;
+
+  // lora_down rows 256b .. 256b+255 ([k][RANK] as stored, contiguous) into
+  // this wave's LDS area with direct loads
+  auto stage_factor = [&](int b) {
+    if constexpr (RANK > 0) {
+      const __amdgpu_buffer_rsrc_t f_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(down + (int64_t)b * 256 * RANK), (short)0, FAC_BYTES, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < FAC_BYTES / 1024; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            f_rsrc, (__attribute__((address_space(3))) void*)(&wave_lds[wave][0] + i * 1024), 16,
+            (uint32_t)(lane * 16 + i * 1024), 0, 0, 0);
+    }
+  };
+
+  uint32_t xb[NB][32];
+  f32x4 acc[RT > 0 ? RT : 1] = {};
+  u16x2 amax2 = (u16x2){0, 0};
+  if (nown > 0) stage_factor(wave);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    if (nb < nown) load_x64(xb[nb], x + lrow * k + (int64_t)(wave + PREP_WAVES * nb) * 256 + 64 * g);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (nb >= nown) break;
+    if constexpr (RANK > 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (nb == 0) {
+        // the staged rows have landed once no more than the x loads issued
+        // behind them are outstanding (loads complete in order)
+        if (NB > 1 && nown > 1) __builtin_amdgcn_s_waitcnt(sq_wait_vm(16));
+        else __builtin_amdgcn_s_waitcnt(sq_wait_vm(8));
+      } else {
+        // the previous block's fragments have been read out of the area
+        // (lgkmcnt 0) before the next block's rows are loaded into it; every
+        // x load was issued first, so the rows have landed at vmcnt 0
+        __builtin_amdgcn_s_waitcnt(SQ_WAIT_LGKM0);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_factor(wave + PREP_WAVES * nb);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(SQ_WAIT_VM0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* st = reinterpret_cast<const uint16_t*>(&wave_lds[wave][0]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 afrag = __builtin_bit_cast(
+            bf16x8, (u32x4){xb[nb][4 * j], xb[nb][4 * j + 1], xb[nb][4 * j + 2], xb[nb][4 * j + 3]});
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          bf16x8 f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            f[e] = __builtin_bit_cast(__bf16, st[(64 * g + 8 * j + e) * RANK + 16 * rt + c]);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, f, acc[rt], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, xb[nb][j] & 0x7FFF7FFFu));
+  }
+
+  // acc[rt][i] = this wave's part of t[row0 + 4g + i][16 rt + c]; the sums go
+  // to the start of the wave's own area (its fragments have been read)
+  __builtin_amdgcn_s_waitcnt(SQ_WAIT_LGKM0);
+  __builtin_amdgcn_sched_barrier(0);
+  auto sums = [&](int w) { return reinterpret_cast<float(*)[RANK > 0 ? RANK : 1]>(&wave_lds[w][0]); };
+  if constexpr (RANK > 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sums(wave)[4 * g + i][16 * rt + c] = acc[rt][i];
+  }
+  red_max[wave][lane] = max((uint32_t)amax2[0], (uint32_t)amax2[1]);
+  __syncthreads();
+  if (tid < 16) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int w = 0; w < PREP_WAVES; ++w)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) mx = max(mx, red_max[w][tid + 16 * gg]);
+    s_exp[tid] = row_exponent(mx);
+    if (row0 + tid < m) rowscale[row0 + tid] = ldexpf(1.0f, s_exp[tid] - 11);
+  }
+  __syncthreads();
+  if constexpr (RANK > 0) {
+    // t summed over the waves in a fixed order, scaled, split into bf16 hi + lo
+    for (int i = tid; i < 16 * RANK; i += 64 * PREP_WAVES) {
+      const int rr = i / RANK, r = i - rr * RANK;
+      const int64_t row = row0 + rr;
+      if (row >= m) continue;
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < PREP_WAVES; ++w) t += sums(w)[rr][r];
+      t *= ldexpf(1.0f, 11 - s_exp[rr]);
+      const uint16_t hb = f32_to_bf16(t);
+      thi[row * RANK + r] = hb;
+      tlo[row * RANK + r] = f32_to_bf16(t - bf16_to_f32(hb));
+    }
+    __syncthreads();   // the sums have been read: the areas take the store staging
+  }
+
+  const float f = ldexpf(1.0f, 11 - s_exp[c]) * 0.0625f;   // exact: a power of two
+  u32x4* stage = reinterpret_cast<u32x4*>(&wave_lds[wave][0]);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(xh + row0 * k), (short)0, (int)(min((int64_t)16, m - row0) * k * 2), 0x00020000);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if (nb >= nown) break;
+    const int64_t b = wave + PREP_WAVES * nb;
+    float v[64];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      v[2 * j] = bf16_to_f32(xb[nb][j] & 0xFFFFu);
+      v[2 * j + 1] = bf16_to_f32(xb[nb][j] >> 16);
+    }
+    fwht_inreg64(v);
+    fwht_cross64_swap(v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const _Float16 lo = (_Float16)(v[8 * j + p] * f);
+        const _Float16 hi = (_Float16)(v[8 * j + p + 4] * f);
+        o[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      }
+      stage[c * PRE_STAGE_U4 + (swap_col(g, 8 * j) >> 3)] = o;
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t off = 2u * ((uint32_t)((lane >> 5) * k) + (uint32_t)(b * 256) + 8u * (lane & 31));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 o = stage[(2 * j + (lane >> 5)) * PRE_STAGE_U4 + (lane & 31)];
+      __builtin_amdgcn_raw_buffer_store_b128(o, rsrc, off + (uint32_t)(4 * j) * (uint32_t)k, 0, 0);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -1012,6 +1196,11 @@ FwdPlan plan_fwd(int64_t m, int64_t n, int64_t k, int group, int rank) {
   // statistics pass: one 256-column block per wave, K slices of four blocks
   p.pre_bps = PRE_WAVES;
   row_stats_plan(m, k, &p.pre_tiles, &p.pre_slices);
+  // one launch for both passes while a strip's blocks fit in the registers
+  // of one workgroup, and the rank's factor rows in its LDS
+  p.pre_fused = 0;
+  if ((rank == 0 || rank == 16 || rank == 32) && k / 256 <= PREP_WAVES * PREP_MAX_NB)
+    p.pre_fused = k / 256 <= PREP_WAVES ? 1 : 2;
   p.off_amax = off;      off = align256(off + (size_t)p.pre_slices * m * 4);
   p.off_tpart = off;     off = align256(off + (size_t)p.pre_slices * m * std::max(rank, 1) * 4);
   const bool partials = p.splits > 1 || p.skinny_mt > 0;
@@ -1071,6 +1260,19 @@ hipError_t launch_fwd_rotate(const FwdPlan& p, const uint16_t* x, const uint16_t
                              void* workspace, hipStream_t stream) {
   const FwdBuffers b = carve(p, workspace);
   hipError_t err;
+  if (p.pre_fused) {
+    const dim3 grid((unsigned)((p.m + 15) / 16));
+#define SQ_PREP(R, NB)                                                                           \
+  hipLaunchKernelGGL((k_fwd_prep<R, NB>), grid, dim3(64 * PREP_WAVES), 0, stream, x, down, p.m, \
+                     p.k, b.xh, b.thi, b.tlo, b.rowscale)
+#define SQ_PREP_NB(R) if (p.pre_fused == 1) SQ_PREP(R, 1); else SQ_PREP(R, 2)
+    if (p.rank == 0) { SQ_PREP_NB(0); }
+    else if (p.rank == 16) { SQ_PREP_NB(16); }
+    else { SQ_PREP_NB(32); }
+#undef SQ_PREP_NB
+#undef SQ_PREP
+    return hipGetLastError();
+  }
   // ranks 16 and 32: the statistics pass reads lora_down as stored; rank 64
   // (whose staged rows would not fit beside the sums) reads a transposed copy
   const bool kmajor = p.rank > 0 && p.rank <= 32;

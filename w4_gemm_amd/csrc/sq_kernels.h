@@ -54,6 +54,7 @@ struct FwdPlan {
   int skinny_kslice;   // its K slice (a multiple of 256)
   int pre_bps, pre_slices;  // 256-column blocks per K slice of the statistics pass, slices
   int pre_tiles;            // 16-row tiles per statistics workgroup (1, 2, 4 or 8)
+  int pre_fused;            // > 0: both pre-phase passes in one launch, this many blocks per wave
   int dec;             // 1: the small-M decode path (rotation inside the contraction)
   int dec_kslice;      // its K slice (a multiple of 256, at most 1024)
   size_t off_xh, off_thi, off_tlo, off_rowscale, off_downT, off_amax, off_tpart, off_partial, total;
