@@ -215,6 +215,74 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_stats(
   }
 }
 
+// Hadamard-256 of a 16-row x 256-column block on the matrix cores.  With
+// the column index k = 32 kh + kl, Sylvester's matrix factors as
+// S256[k][n] = S8[kh][nh] S32[kl][nl] (n = 32 nh + nl), so
+//   1. per 32-column chunk kh, two bf16 MFMAs against S32 (entries +-1: the
+//      products are exact, the sums fp32) give Y[kh][nl] = sum_kl x[32kh+kl] S32[kl][nl];
+//   2. the 8-point transform over kh runs in each lane's registers.
+// A operand: lane (c, g) holds xf[kh] = x[row c][32 kh + 8g .. +7], the
+// statistics pass's layout.  The S32 columns are ordered so that output
+// column c' of half h is nl = fwht_out_col(h, c') = 8 (c' >> 2) + (c' & 3) + 4h:
+// a lane then holds both columns of one word of the xh layout (word p of every
+// 8-column run holds columns p and p + 4).
+// Result: z[h][nh][i] = (S256 x)[row 4g + i][32 nh + fwht_out_col(h, c)].
+__device__ __forceinline__ int fwht_out_col(int h, int cc) { return 8 * (cc >> 2) + (cc & 3) + 4 * h; }
+
+__device__ __forceinline__ void s32_fragments(bf16x8 (&s)[2], int lane) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      s[h][e] = (__builtin_popcount((8 * g + e) & fwht_out_col(h, c)) & 1) ? (__bf16)-1.0f : (__bf16)1.0f;
+}
+
+__device__ __forceinline__ void fwht256_mfma(const bf16x8 (&xf)[8], const bf16x8 (&s)[2],
+                                             f32x4 (&z)[2][8]) {
+#pragma unroll
+  for (int kh = 0; kh < 8; ++kh)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      z[h][kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[kh], s[h], (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+  for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+    for (int kh = 0; kh < 8; ++kh) {
+      if (kh & st) continue;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = z[h][kh][i], b = z[h][kh + st][i];
+          z[h][kh][i] = a + b;
+          z[h][kh + st][i] = a - b;
+        }
+    }
+}
+
+// Scale rows 4g + i by f[i], round to fp16 and store the block: the word of
+// (z[0], z[1]) goes to byte 64 nh + 4c of the block's 512-byte segment of
+// strip row 4g + i, so 16 lanes write 64 contiguous bytes of a row.  `base` is
+// the block's byte offset in row 0 of the strip; the descriptor ends at row
+// m, so rows of a ragged last strip are dropped by its range check.
+__device__ __forceinline__ void store_xh_block(const f32x4 (&z)[2][8], const float (&f)[4],
+                                               __amdgpu_buffer_rsrc_t rsrc, uint32_t base,
+                                               uint32_t row_bytes, int lane) {
+  const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int nh = 0; nh < 8; ++nh) {
+      const _Float16 lo = (_Float16)(z[0][nh][i] * f[i]);
+      const _Float16 hi = (_Float16)(z[1][nh][i] * f[i]);
+      const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
+                         ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      __builtin_amdgcn_raw_buffer_store_b32(
+          w, rsrc, base + (uint32_t)(4 * g + i) * row_bytes + (uint32_t)(64 * nh + 4 * c), 0, 0);
+    }
+}
+
 // Pass 2: grid (ceil(m/16), ceil(nblk/4)); wave w of workgroup (i, j) owns
 // rows 16i.. and the 256-column block 4j + w.
 __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
@@ -304,14 +372,12 @@ __global__ void __launch_bounds__(64 * PRE_WAVES) k_fwd_rotate(
 // Both passes in one launch, for K <= 256 * PREP_WAVES * NB and ranks 0, 16
 // and 32: workgroup i owns rows 16i .. 16i+15 over all of K, and wave w the
 // 256-column blocks w, w + PREP_WAVES, ... (at most NB of them), whose x it
-// loads once, in the rotation's lane layout (lane (c, g): row c, columns
-// 64g .. 64g+63), and keeps in registers.  The t MFMAs take their K slots in
-// that layout too: slot (g, e) of MFMA j is column 64g + 8j + e of the block,
-// for x (A) and for the staged lora_down rows (B) alike, so the sum is the
-// same dot product over the block.  The row maxima and the waves' t sums meet
-// in LDS; then every wave rotates its blocks from registers and stores them
-// as the rotation pass does.  At these sizes the two passes are two short
-// launches, each mostly latency.
+// loads once, in the statistics pass's layout.  Per block the wave takes the
+// row maxima, t on MFMA against its block's staged lora_down rows, and the
+// Hadamard transform (fwht256_mfma) before any row scale is known; the
+// maxima and the waves' t sums then meet in LDS, and every wave scales,
+// rounds and stores its blocks.  At these sizes the two passes would be two
+// short launches, each mostly latency.
 constexpr int PREP_WAVES = 8;
 constexpr int PREP_MAX_NB = 2;
 
@@ -323,11 +389,9 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) k_fwd_prep(
   static_assert(RANK == 0 || RANK == 16 || RANK == 32, "staged factor: ranks 16 and 32");
   static_assert(NB >= 1 && NB <= PREP_MAX_NB, "blocks per wave");
   constexpr int RT = RANK / 16;
-  constexpr int STAGE_BYTES = 16 * PRE_STAGE_U4 * 16;   // the store staging of one block
-  constexpr int FAC_BYTES = 256 * RANK * 2;              // one block's lora_down rows
+  constexpr int FAC_BYTES = 256 * RANK * 2;   // one block's lora_down rows
   constexpr int SUM_BYTES = 16 * (RANK > 0 ? RANK : 1) * 4;
-  constexpr int WAVE_LDS = STAGE_BYTES > FAC_BYTES ? (STAGE_BYTES > SUM_BYTES ? STAGE_BYTES : SUM_BYTES)
-                                                   : (FAC_BYTES > SUM_BYTES ? FAC_BYTES : SUM_BYTES);
+  constexpr int WAVE_LDS = FAC_BYTES > SUM_BYTES ? FAC_BYTES : SUM_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t wave_lds[PREP_WAVES][WAVE_LDS];
   __shared__ uint32_t red_max[PREP_WAVES][64];
   __shared__ int s_exp[16];
@@ -353,15 +417,26 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) k_fwd_prep(
     }
   };
 
-  uint32_t xb[NB][32];
-  f32x4 acc[RT > 0 ? RT : 1] = {};
-  u16x2 amax2 = (u16x2){0, 0};
+  // the first block's factor rows, then every owned block of x (eight
+  // 16-byte loads per block: columns 32j + 8g .. +7 of row c)
+  bf16x8 xf[NB][8];
   if (nown > 0) stage_factor(wave);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
-    if (nb < nown) load_x64(xb[nb], x + lrow * k + (int64_t)(wave + PREP_WAVES * nb) * 256 + 64 * g);
+    if (nb < nown) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        xf[nb][j] = *reinterpret_cast<const bf16x8*>(
+            x + lrow * k + (int64_t)(wave + PREP_WAVES * nb) * 256 + 32 * j + 8 * g);
+    }
   __builtin_amdgcn_sched_barrier(0);
+
+  bf16x8 s32[2];
+  s32_fragments(s32, lane);
+  f32x4 acc[RT > 0 ? RT : 1] = {};
+  f32x4 z[NB][2][8];
+  u16x2 amax2 = (u16x2){0, 0};
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     if (nb >= nown) break;
@@ -383,24 +458,27 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) k_fwd_prep(
         __builtin_amdgcn_s_waitcnt(SQ_WAIT_VM0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      // B element e of fragment (rt, j): lora_down row 32j + 8g + e, column 16rt + c
       const uint16_t* st = reinterpret_cast<const uint16_t*>(&wave_lds[wave][0]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bf16x8 afrag = __builtin_bit_cast(
-            bf16x8, (u32x4){xb[nb][4 * j], xb[nb][4 * j + 1], xb[nb][4 * j + 2], xb[nb][4 * j + 3]});
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           bf16x8 f;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            f[e] = __builtin_bit_cast(__bf16, st[(64 * g + 8 * j + e) * RANK + 16 * rt + c]);
-          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag, f, acc[rt], 0, 0, 0);
+            f[e] = __builtin_bit_cast(__bf16, st[(32 * j + 8 * g + e) * RANK + 16 * rt + c]);
+          acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[nb][j], f, acc[rt], 0, 0, 0);
         }
-      }
     }
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-      amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, xb[nb][j] & 0x7FFF7FFFu));
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 w = __builtin_bit_cast(u32x4, xf[nb][j]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax2 = __builtin_elementwise_max(amax2, __builtin_bit_cast(u16x2, w[e] & 0x7FFF7FFFu));
+    }
+    fwht256_mfma(xf[nb], s32, z[nb]);
   }
 
   // acc[rt][i] = this wave's part of t[row0 + 4g + i][16 rt + c]; the sums go
@@ -440,47 +518,17 @@ __global__ void __launch_bounds__(64 * PREP_WAVES) k_fwd_prep(
       thi[row * RANK + r] = hb;
       tlo[row * RANK + r] = f32_to_bf16(t - bf16_to_f32(hb));
     }
-    __syncthreads();   // the sums have been read: the areas take the store staging
   }
 
-  const float f = ldexpf(1.0f, 11 - s_exp[c]) * 0.0625f;   // exact: a power of two
-  u32x4* stage = reinterpret_cast<u32x4*>(&wave_lds[wave][0]);
+  float f[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = ldexpf(1.0f, 11 - s_exp[4 * g + i]) * 0.0625f;   // exact
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(xh + row0 * k), (short)0, (int)(min((int64_t)16, m - row0) * k * 2), 0x00020000);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     if (nb >= nown) break;
-    const int64_t b = wave + PREP_WAVES * nb;
-    float v[64];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      v[2 * j] = bf16_to_f32(xb[nb][j] & 0xFFFFu);
-      v[2 * j + 1] = bf16_to_f32(xb[nb][j] >> 16);
-    }
-    fwht_inreg64(v);
-    fwht_cross64_swap(v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const _Float16 lo = (_Float16)(v[8 * j + p] * f);
-        const _Float16 hi = (_Float16)(v[8 * j + p + 4] * f);
-        o[p] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-      }
-      stage[c * PRE_STAGE_U4 + (swap_col(g, 8 * j) >> 3)] = o;
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_wave_barrier();
-    const uint32_t off = 2u * ((uint32_t)((lane >> 5) * k) + (uint32_t)(b * 256) + 8u * (lane & 31));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 o = stage[(2 * j + (lane >> 5)) * PRE_STAGE_U4 + (lane & 31)];
-      __builtin_amdgcn_raw_buffer_store_b128(o, rsrc, off + (uint32_t)(4 * j) * (uint32_t)k, 0, 0);
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_wave_barrier();
+    store_xh_block(z[nb], f, rsrc, (uint32_t)((wave + PREP_WAVES * nb) * 512), (uint32_t)(k * 2), lane);
   }
 }
 
