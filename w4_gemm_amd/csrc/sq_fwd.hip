@@ -1276,13 +1276,20 @@ static FwdBuffers carve(const FwdPlan& p, void* workspace) {
                     reinterpret_cast<float*>(ws + p.off_tpart)};
 }
 
-// Row tiles per statistics workgroup: as many as still leave 256 workgroups.
+// Row tiles per statistics workgroup: the most that still fill the chip in
+// one resident round (256 to 512 workgroups: at rank 32 a workgroup's staged
+// factor rows take 66 KB of LDS, so two fit per CU), else two.  With more
+// workgroups than resident slots, long-running many-tile workgroups leave a
+// near-empty second round (4480 x 16384: 560 workgroups of eight tiles
+// measured 6 us slower than 2240 of two).
 void row_stats_plan(int64_t m, int64_t k, int* tiles, int* slices) {
   const int64_t strips = (m + 15) / 16, nblk = k / 256;
   *slices = (int)((nblk + PRE_WAVES - 1) / PRE_WAVES);
   *tiles = 1;
-  for (int t : {8, 4, 2})
-    if (((strips + t - 1) / t) * *slices >= 256) { *tiles = t; break; }
+  for (int t : {8, 4, 2}) {
+    const int64_t wgs = ((strips + t - 1) / t) * *slices;
+    if (wgs >= 256 && (wgs <= 512 || t == 2)) { *tiles = t; break; }
+  }
 }
 
 hipError_t launch_row_stats(const uint16_t* a, const uint16_t* fac, bool kmajor, int64_t m,
