@@ -217,13 +217,14 @@ def test_fwd_mid_m_plans():
 
 
 def test_fwd_statistics_tile_plans():
-    # long K and many rows: the statistics pass takes four and eight 16-row
-    # tiles per workgroup (at rank 64 with two x tiles in flight, at rank 32
-    # with two and four), with a ragged last row tile
+    # long K and many rows: the statistics pass takes two, four and eight
+    # 16-row tiles per workgroup (at rank 64 with two x tiles in flight, at
+    # rank 32 with two and four), with a ragged last row tile; 4480 rows take
+    # two tiles (eight would need more workgroups than fit at once)
     rng = np.random.default_rng(13)
     from synth import gen_activations
     for (m, n, k, rank) in [(1000, 256, 16384, 64), (2040, 300, 16384, 64), (1000, 256, 16384, 32),
-                            (2040, 300, 16384, 32)]:
+                            (2040, 300, 16384, 32), (4470, 260, 16384, 64)]:
         codes, scales, upb, dnb = gen_payload(rng, n, k, 32, rank)
         xbits = gen_activations(rng, m, k, 0.01)
         rows = np.sort(np.concatenate([rng.choice(m - 1, 15, replace=False), [m - 1]]))
